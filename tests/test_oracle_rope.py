@@ -1,0 +1,121 @@
+"""Oracle RoPE: closed forms, the multiplicative identity and invariants.
+
+The identity e^{i theta p} e^{i theta delta} = e^{i theta (p+delta)} is stated in
+the digest (前置知识 RoPE) and in the arXiv HTML ("Incremental RoPE adjustment");
+the shift rotates only the 44 temporal dims (1_h, 1_w are identities).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+
+def _max_identity_error(shift_fn, encode_fn, seed=0, trials=200):
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for _ in range(trials):
+        k = rng.standard_normal((3, O.HEAD_DIM))
+        p = (int(rng.integers(0, 480)), int(rng.integers(0, 60)), int(rng.integers(0, 104)))
+        d = int(rng.integers(-480, 481))
+        lhs = shift_fn(encode_fn(k, *p), d)
+        rhs = encode_fn(k, p[0] + d, p[1], p[2])
+        worst = max(worst, float(np.max(np.abs(lhs - rhs))))
+    return worst
+
+
+def test_incremental_shift_equals_reencode():
+    err = _max_identity_error(O.rope_shift, O.rope_encode)
+    assert err <= 1e-6
+    assert err < 1e-10  # the actual fp64 error is ~1e-13
+
+
+def test_closed_form_rotation():
+    # theta_{t,0} = base^0 = 1, so p_t = 1 rotates pair 0 by one radian, and
+    # p_t = pi/2 takes (1, 0) to (0, 1): the positive sense of e^{+i theta p}.
+    e0 = np.zeros(O.HEAD_DIM)
+    e0[0] = 1.0
+    r = O.rope_encode(e0, 1.0, 0.0, 0.0)
+    assert r[0] == pytest.approx(0.5403023058681398, abs=1e-15)
+    assert r[1] == pytest.approx(0.8414709848078965, abs=1e-15)
+    r = O.rope_encode(e0, math.pi / 2, 0.0, 0.0)
+    assert abs(r[0]) < 1e-15 and r[1] == pytest.approx(1.0, abs=1e-15)
+    # height and width axes start at dims 44 and 86
+    for start, pos in ((44, (0, 1, 0)), (86, (0, 0, 1))):
+        e = np.zeros(O.HEAD_DIM)
+        e[start] = 1.0
+        r = O.rope_encode(e, *map(float, pos))
+        assert r[start] == pytest.approx(0.5403023058681398, abs=1e-15)
+        assert r[start + 1] == pytest.approx(0.8414709848078965, abs=1e-15)
+        assert np.count_nonzero(r) == 2
+
+
+def test_relative_position_property():
+    # Textbook RoPE: <enc(q, p1), enc(k, p2)> depends only on p1 - p2 per axis.
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal((2, O.HEAD_DIM))
+    a = O.rope_encode(q, 17, 5, 9) @ O.rope_encode(k, 4, 2, 30)
+    b = O.rope_encode(q, 117, 25, 19) @ O.rope_encode(k, 104, 22, 40)
+    assert a == pytest.approx(b, abs=1e-11)
+    c = O.rope_encode(q, 18, 5, 9) @ O.rope_encode(k, 4, 2, 30)
+    assert abs(a - c) > 1e-6
+
+
+def test_shift_touches_only_temporal_dims_and_preserves_norms():
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((64, O.HEAD_DIM))
+    s = O.rope_shift(k, 37.0)
+    assert np.array_equal(s[:, 44:], k[:, 44:])
+    n0 = np.hypot(k[:, 0:44:2], k[:, 1:44:2])
+    n1 = np.hypot(s[:, 0:44:2], s[:, 1:44:2])
+    assert np.max(np.abs(n0 - n1)) < 1e-12
+    back = O.rope_shift(s, -37.0)
+    assert np.max(np.abs(back - k)) < 1e-12
+
+
+def test_shift_blocks_bf16_storage():
+    rng = np.random.default_rng(5)
+    n_c, H = 8, 2
+    pool = O.f64_to_bf16(rng.standard_normal((10 * n_c, H, O.HEAD_DIM)))
+    same = O.rope_shift_blocks(pool, n_c, [1, 4], [0, 0])
+    assert np.array_equal(same, pool)                    # delta = 0 is bitwise identity
+    out = O.rope_shift_blocks(pool, n_c, [1, 4], [7, 20])
+    assert np.array_equal(out[..., 44:], pool[..., 44:])  # dims 44..127 bitwise unchanged
+    untouched = np.ones(10 * n_c, bool)
+    untouched[n_c:2 * n_c] = untouched[4 * n_c:5 * n_c] = False
+    assert np.array_equal(out[untouched], pool[untouched])
+    # each stored value is the bf16 rounding of the exact rotation
+    exact = O.rope_shift(O.bf16_to_f64(pool[n_c:2 * n_c]), 7.0)
+    assert np.array_equal(out[n_c:2 * n_c], O.f64_to_bf16(exact))
+
+
+def _mut_sign(k, d):
+    return O.rope_shift(k, -d)
+
+
+def _mut_all_dims(k, d):
+    return O.rope_encode(k, d, d, d)
+
+
+def _mut_freq(k, d):
+    k = np.array(k, dtype=np.float64, copy=True)
+    j = np.arange(22)
+    th = O.ROPE_BASE ** (-2.0 * (j + 1) / 44)       # off-by-one frequency index
+    z = (k[..., 0:44:2] + 1j * k[..., 1:44:2]) * np.exp(1j * th * d)
+    k[..., 0:44:2], k[..., 1:44:2] = z.real, z.imag
+    return k
+
+
+def _mut_pairing(k, d):
+    k = np.array(k, dtype=np.float64, copy=True)
+    j = np.arange(22)
+    th = O.ROPE_BASE ** (-2.0 * j / 44)
+    z = (k[..., 0:22] + 1j * k[..., 22:44]) * np.exp(1j * th * d)   # split-half pairs
+    k[..., 0:22], k[..., 22:44] = z.real, z.imag
+    return k
+
+
+@pytest.mark.parametrize("mutant", [_mut_sign, _mut_all_dims, _mut_freq, _mut_pairing])
+def test_planted_mistakes_fail_identity(mutant):
+    assert _max_identity_error(mutant, O.rope_encode, trials=20) > 1e-3

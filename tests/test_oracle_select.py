@@ -1,0 +1,108 @@
+"""Oracle selection and placement.
+
+Selection: query-key affinity over compressed mid blocks, top-k
+[digest 方法步骤详情 (3); arXiv "Compressed Mid Tokens"]. The block score is the
+stated reading: mean over heads of <mean-pooled Q, mean-pooled block keys>/sqrt(128).
+Placement: the selected blocks are re-aligned to continuous positions
+[summary "Method"; arXiv "Incremental RoPE adjustment"].
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import pfgen
+
+
+def test_planted_answer_is_recovered():
+    cfg = pfgen.C0.replace(pool_blocks=24, top_k=5)
+    chosen = [2, 7, 11, 19, 23]
+    c = pfgen.planted_pool(cfg, 11, chosen)
+    s = O.block_scores(c["q"], c["pool_k"], cfg.n_c)
+    assert O.select_topk(s, 5) == chosen
+    assert O.topk_gap(s, 5) > 1.0
+
+
+def test_double_sum_definition_tiny():
+    # phi_j = sum_h sum_i sum_{t in block j} q_i . k_t / sqrt(128), in loops; it
+    # equals n_q * N_c * H * s_j, so it ranks blocks identically.
+    rng = np.random.default_rng(12)
+    n_q, n_c, M, H = 4, 3, 5, 2
+    q = O.f64_to_bf16(rng.standard_normal((n_q, H, 128)))
+    kp = O.f64_to_bf16(rng.standard_normal((M * n_c, H, 128)))
+    Q, K = O.bf16_to_f64(q).tolist(), O.bf16_to_f64(kp).tolist()
+    s = O.block_scores(q, kp, n_c)
+    for j in range(M):
+        phi = 0.0
+        for h in range(H):
+            for i in range(n_q):
+                for t in range(j * n_c, (j + 1) * n_c):
+                    phi += sum(a * b for a, b in zip(Q[i][h], K[t][h])) / math.sqrt(128)
+        assert phi == pytest.approx(n_q * n_c * H * s[j], rel=1e-12, abs=1e-12)
+
+
+def test_ties_go_to_lower_index():
+    cfg = pfgen.C0
+    c = pfgen.make(cfg)
+    pk = c["pool_k"].copy()
+    s = O.block_scores(c["q"], pk, cfg.n_c)
+    best = int(np.argmax(s))
+    dup = (best + 5) % cfg.pool_blocks
+    pk[dup * 8:(dup + 1) * 8] = pk[best * 8:(best + 1) * 8]
+    s2 = O.block_scores(c["q"], pk, cfg.n_c)
+    assert s2[best] == s2[dup]
+    assert O.select_topk(s2, 1) == [min(best, dup)]
+    assert O.select_topk([1.0, 2.0, 2.0, 0.5], 2) == [1, 2]
+    assert O.select_topk([2.0, 2.0, 2.0, 2.0], 3) == [0, 1, 2]
+
+
+def test_k_equals_m_and_order():
+    s = [0.3, -1.0, 5.0, 0.2]
+    assert O.select_topk(s, 4) == [0, 1, 2, 3]
+    assert O.select_topk(s, 2) == [0, 2]         # ascending block order
+    assert O.topk_gap(s, 4) == math.inf
+    assert O.topk_gap(s, 2) == pytest.approx(0.1)
+
+
+def test_acceptable_sets():
+    s = [1.0, 0.9995, 0.5, 0.2]
+    assert O.topk_acceptable([0], s, 1, 1e-3)
+    assert O.topk_acceptable([1], s, 1, 1e-3)      # within the near-tie window
+    assert not O.topk_acceptable([2], s, 1, 1e-3)
+    assert not O.topk_acceptable([0, 0], s, 2, 1e-3)
+
+
+def test_placement_closed_form_first_use():
+    M, k, Bf, Sb = 40, 16, 4, 2
+    tags = O.initial_pos_tags(M, Sb, Bf)
+    assert list(tags[:3]) == [8, 12, 16]             # sink holds frames 0..7
+    rng = np.random.default_rng(0)
+    ids = sorted(rng.choice(M, k, replace=False).tolist())
+    Fr = (Sb + M) * Bf
+    d, t = O.placement_deltas(ids, tags, Fr, Bf)
+    for r, b in enumerate(ids):
+        assert d[r] == (M - k + r - b) * Bf          # closed form from the initial tags
+        assert d[r] >= 0
+    sel = t[ids]
+    assert list(np.diff(sel)) == [Bf] * (k - 1) and sel[-1] + Bf == Fr
+    # selecting the newest k blocks needs no shift
+    d2, _ = O.placement_deltas(list(range(M - k, M)), tags, Fr, Bf)
+    assert not d2.any()
+
+
+def test_placement_repeated_keeps_tags_consistent():
+    M, k, Bf, Sb = 12, 4, 4, 2
+    tags0 = O.initial_pos_tags(M, Sb, Bf)
+    tags = tags0.copy()
+    total = np.zeros(M, np.int64)
+    Fr = (Sb + M) * Bf
+    rng = np.random.default_rng(1)
+    saw_negative = False
+    for _ in range(6):
+        ids = sorted(rng.choice(M, k, replace=False).tolist())
+        d, tags = O.placement_deltas(ids, tags, Fr, Bf)
+        total[ids] += d
+        saw_negative |= bool((d < 0).any())
+    assert np.array_equal(tags0 + total, tags)       # a tag is its start plus every shift
+    assert saw_negative                               # later steps can move blocks back
