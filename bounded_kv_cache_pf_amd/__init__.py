@@ -1,0 +1,202 @@
+"""Python binding of libpf (PackForcing partition attention on MI355X).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C ABI declared in include/pf.h, and every step
+runs in libpf's HIP kernels. torch supplies device memory and streams.
+
+Tensors are torch CUDA tensors laid out [rows][heads][128], dtype bfloat16
+(or int16 holding bfloat16 bits); index arrays are int32. If libpf.so has not
+been built, importing this package raises ImportError: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpf.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bounded_kv_cache_pf_amd.build` "
+                      "(or __graft_entry__.build()); the package has no CPU fallback")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "pf_abi_version": ([], ctypes.c_int),
+    "pf_status_name": ([_i32], ctypes.c_char_p),
+    "pf_last_error_message": ([], ctypes.c_char_p),
+    "pf_score_select_workspace_bytes": ([_i64, _i32, _i32, _i32], _sz),
+    "pf_score_select": ([_p, _i64, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _sz, _p], _i32),
+    "pf_selection_deltas": ([_p, _i32, _p, _i32, ctypes.c_int32, ctypes.c_int32, _p, _p], _i32),
+    "pf_rope_shift": ([_p, _i32, _i64, _i64, _p, _p, _i32, ctypes.c_double, _p], _i32),
+    "pf_partition_attn_workspace_bytes": ([_i64, _i32, _i64], _sz),
+    "pf_partition_attn": ([_p, _i64, _i32,
+                           _p, _p, _i64,
+                           _p, _p, _i32, _i32, _p, _i32,
+                           _p, _p, _i64,
+                           _p, _p, _i64,
+                           ctypes.c_float, _p, _p, _p, _sz, _p], _i32),
+}
+for _name, (_args, _ret) in _SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _ret
+
+PF_OK = 0
+HEAD_DIM = 128
+
+
+class PFError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = lib.pf_status_name(status).decode()
+        msg = lib.pf_last_error_message().decode()
+        super().__init__(f"{where}: {name}: {msg}")
+        self.name = name
+
+
+def _check(status: int, where: str) -> None:
+    if status != PF_OK:
+        raise PFError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _kv_rows(t, heads: int, what: str) -> int:
+    torch = _torch()
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16):
+        raise TypeError(f"{what} must be bfloat16 (or int16 bf16 bits), got {t.dtype}")
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != HEAD_DIM or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous [rows][{heads}][128] tensor, got {tuple(t.shape)}")
+    return int(t.shape[0])
+
+
+def _i32_vec(t, what: str) -> None:
+    torch = _torch()
+    if t is None:
+        return
+    if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{what} must be a contiguous int32 CUDA tensor")
+
+
+def pf_score_select_workspace_bytes(n_q: int, n_heads: int, n_blocks: int, n_c: int) -> int:
+    return int(lib.pf_score_select_workspace_bytes(n_q, n_heads, n_blocks, n_c))
+
+
+def pf_score_select(q, pool_k, n_c: int, top_k: int, ids_out=None, scores_out=None, workspace=None,
+                    stream=None) -> Tuple[object, object]:
+    """Top-k pool blocks by pooled query-key affinity. Returns (ids int32[top_k], scores f32[n_blocks])."""
+    torch = _torch()
+    heads = int(q.shape[1])
+    n_q = _kv_rows(q, heads, "q")
+    rows = _kv_rows(pool_k, heads, "pool_k")
+    if n_c <= 0 or rows % n_c:
+        raise ValueError("pool rows must be a multiple of n_c")
+    n_blocks = rows // n_c
+    if ids_out is None:
+        ids_out = torch.empty(top_k, dtype=torch.int32, device=q.device)
+    if scores_out is None:
+        scores_out = torch.empty(n_blocks, dtype=torch.float32, device=q.device)
+    _i32_vec(ids_out, "ids_out")
+    need = pf_score_select_workspace_bytes(n_q, heads, n_blocks, n_c)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.pf_score_select(_ptr(q), n_q, heads, _ptr(pool_k), n_blocks, n_c, top_k, _ptr(ids_out),
+                               _ptr(scores_out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "pf_score_select")
+    return ids_out, scores_out
+
+
+def pf_selection_deltas(ids, pos_tags, recent_first_frame: int, block_frames: int, deltas_out=None,
+                        stream=None):
+    """Per-block temporal shift placing the selected blocks before the recent block; updates pos_tags."""
+    torch = _torch()
+    _i32_vec(ids, "ids")
+    _i32_vec(pos_tags, "pos_tags")
+    if deltas_out is None:
+        deltas_out = torch.empty(ids.numel(), dtype=torch.int32, device=ids.device)
+    _i32_vec(deltas_out, "deltas_out")
+    _check(lib.pf_selection_deltas(_ptr(ids), ids.numel(), _ptr(pos_tags), pos_tags.numel(),
+                                   recent_first_frame, block_frames, _ptr(deltas_out), _stream(stream)),
+           "pf_selection_deltas")
+    return deltas_out
+
+
+def pf_rope_shift(k, rows_per_block: int, deltas, block_ids=None, rope_base: float = 10000.0, stream=None):
+    """Rotate the temporal dims of the listed blocks of k in place by their deltas."""
+    heads = int(k.shape[1])
+    rows = _kv_rows(k, heads, "k")
+    if rows_per_block <= 0 or rows % rows_per_block:
+        raise ValueError("k rows must be a multiple of rows_per_block")
+    _i32_vec(deltas, "deltas")
+    _i32_vec(block_ids, "block_ids")
+    n_shift = deltas.numel()
+    if block_ids is not None and block_ids.numel() != n_shift:
+        raise ValueError("block_ids and deltas differ in length")
+    _check(lib.pf_rope_shift(_ptr(k), heads, rows_per_block, rows // rows_per_block, _ptr(block_ids),
+                             _ptr(deltas), n_shift, rope_base, _stream(stream)), "pf_rope_shift")
+    return k
+
+
+def pf_partition_attn(q, sink_k, sink_v, pool_k, pool_v, n_c: int, mid_ids, recent_k, recent_v, cur_k, cur_v,
+                      scale: float = 0.0, o=None, lse=None, want_lse: bool = False, stream=None):
+    """softmax(scale Q K^T) V over sink || pool[mid_ids] || recent || cur. Returns (o, lse or None)."""
+    torch = _torch()
+    heads = int(q.shape[1])
+    n_q = _kv_rows(q, heads, "q")
+    n_sink = _kv_rows(sink_k, heads, "sink_k")
+    if _kv_rows(sink_v, heads, "sink_v") != n_sink:
+        raise ValueError("sink_k and sink_v differ in rows")
+    n_rec = _kv_rows(recent_k, heads, "recent_k")
+    if _kv_rows(recent_v, heads, "recent_v") != n_rec:
+        raise ValueError("recent_k and recent_v differ in rows")
+    n_cur = _kv_rows(cur_k, heads, "cur_k")
+    if _kv_rows(cur_v, heads, "cur_v") != n_cur:
+        raise ValueError("cur_k and cur_v differ in rows")
+    n_sel = 0 if mid_ids is None else mid_ids.numel()
+    n_blocks = 0
+    if n_sel:
+        _i32_vec(mid_ids, "mid_ids")
+        rows = _kv_rows(pool_k, heads, "pool_k")
+        if _kv_rows(pool_v, heads, "pool_v") != rows or rows % n_c:
+            raise ValueError("pool_k/pool_v rows must match and be a multiple of n_c")
+        n_blocks = rows // n_c
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((heads, n_q), dtype=torch.float32, device=q.device)
+    need = int(lib.pf_partition_attn_workspace_bytes(n_q, heads, n_sink + n_sel * n_c + n_rec + n_cur))
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    _check(lib.pf_partition_attn(_ptr(q), n_q, heads,
+                                 _ptr(sink_k), _ptr(sink_v), n_sink,
+                                 _ptr(pool_k) if n_sel else None, _ptr(pool_v) if n_sel else None, n_blocks,
+                                 n_c, _ptr(mid_ids) if n_sel else None, n_sel,
+                                 _ptr(recent_k), _ptr(recent_v), n_rec,
+                                 _ptr(cur_k), _ptr(cur_v), n_cur,
+                                 float(scale), _ptr(o), _ptr(lse), _ptr(ws), need, _stream(stream)),
+           "pf_partition_attn")
+    return o, lse

@@ -1,0 +1,200 @@
+/*
+ * pf.h — C ABI of libpf: PackForcing per-block context attention on MI355X (gfx950).
+ *
+ * The current block's queries attend over a bounded three-partition KV cache
+ *   C = C_sink || C_mid || C_rc
+ * [PackForcing digest (paper.rainbus.top), 方法步骤详情 (5); PackForcing arXiv
+ * HTML, "Bounded Attention Context"]. The sink and recent/current partitions are
+ * full resolution; the mid partition is the top-k of a pool of compressed blocks,
+ * chosen by query-key affinity [digest, 方法步骤详情 (3); arXiv HTML, "Compressed
+ * Mid Tokens"], whose keys are re-aligned by a temporal-only RoPE rotation
+ * [digest, 方法步骤详情 (4); arXiv HTML, "Incremental RoPE adjustment"].
+ *
+ * Conventions shared by every call:
+ *  - K, V, Q and O are bfloat16, passed as raw 16-bit patterns (pf_bf16).
+ *  - Layout is row-major [rows][n_heads][128]: one row per token, row stride
+ *    n_heads*128 elements. The head dimension is fixed at 128
+ *    (44 temporal + 42 height + 42 width RoPE dims [digest, 前置知识 RoPE]).
+ *  - A pool of compressed blocks is [n_blocks*n_c][n_heads][128]; block j owns
+ *    rows j*n_c .. j*n_c + n_c - 1.
+ *  - Every data pointer is a DEVICE pointer and must be 16-byte aligned.
+ *    Ownership stays with the caller; libpf allocates nothing and keeps no
+ *    device state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work and return; there is no host synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued. On error
+ *    nothing is enqueued, the call returns a pf_status other than PF_OK, and
+ *    pf_last_error_message() describes it. Faults inside a kernel surface at
+ *    the caller's next synchronisation.
+ *  - Index arrays that live on the device (ids, block lists) cannot be checked
+ *    on the host; the kernels skip out-of-range entries instead of reading out
+ *    of bounds, as documented per call.
+ *  - Calls on disjoint buffers may run concurrently. pf_rope_shift and
+ *    pf_selection_deltas write in place: order them against readers of the same
+ *    buffers on the caller's streams.
+ */
+#ifndef PF_H_
+#define PF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PF_ABI_VERSION 1
+#define PF_HEAD_DIM 128
+#define PF_TEMPORAL_DIMS 44
+#define PF_MAX_HEADS 32
+#define PF_MAX_BLOCKS 4096   /* pool blocks scored by pf_score_select */
+#define PF_MAX_TOPK 256      /* top_k of pf_score_select */
+#define PF_MAX_SELECTED 1024 /* n_sel of pf_partition_attn */
+
+typedef uint16_t pf_bf16;
+
+typedef enum pf_status {
+  PF_OK = 0,
+  PF_ERR_NULL = 1,        /* a required pointer is NULL */
+  PF_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
+  PF_ERR_UNSUPPORTED = 3, /* a size beyond the limits above */
+  PF_ERR_MISALIGNED = 4,  /* a data pointer is not 16-byte aligned */
+  PF_ERR_RANGE = 5,       /* a count outside its allowed range (top_k, n_sel, ...) */
+  PF_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the query function says */
+  PF_ERR_HIP = 7          /* the HIP runtime refused a launch; the message names the error */
+} pf_status;
+
+/* PF_ABI_VERSION of the loaded library. */
+int pf_abi_version(void);
+
+/* Static name of a status code ("PF_OK", ...); "PF_UNKNOWN" for other values. */
+const char* pf_status_name(int status);
+
+/* Message of the last failed call on this host thread (empty after a success).
+ * The string is owned by libpf and valid until the thread's next pf_* call. */
+const char* pf_last_error_message(void);
+
+/* ------------------------------------------------------------------------- *
+ * Dynamic context selection
+ * [PackForcing digest, 方法步骤详情 (3): top-K over the compressed mid blocks by
+ *  query-key affinity phi_j = sum_i q_i^T k_j / sqrt(d), N_top = 16;
+ *  arXiv HTML, "Compressed Mid Tokens" and "Implementation Details"]
+ *
+ * The pages leave the pooling open; this library computes, per pool block j,
+ *   s_j = (1/H) sum_h < mean_i Q[i,h,:], mean_{r<n_c} K[j*n_c + r,h,:] > / sqrt(128)
+ * which ranks blocks exactly as the double sum over queries and block keys does.
+ * The k largest s_j are selected, ties going to the lower block index, and
+ * written to ids_out[0..top_k) in ascending block order.
+ *
+ *   q           [n_q][n_heads][128] bf16 — the current block's queries.
+ *   pool_k      [n_blocks*n_c][n_heads][128] bf16 — compressed mid keys.
+ *   ids_out     int32[top_k] (device) — selected block ids, ascending.
+ *   scores_out  float[n_blocks] (device) or NULL — s_j in fp32.
+ *   workspace   device scratch of at least pf_score_select_workspace_bytes(...)
+ *               bytes; its contents need no initialisation.
+ * Limits: 1 <= n_heads <= PF_MAX_HEADS, 1 <= n_blocks <= PF_MAX_BLOCKS,
+ *         1 <= top_k <= min(n_blocks, PF_MAX_TOPK), n_q >= 1, n_c >= 1.
+ * Arithmetic: bf16 inputs, fp32 sums in a fixed order (repeatable bit for bit).
+ * ------------------------------------------------------------------------- */
+size_t pf_score_select_workspace_bytes(int64_t n_q, int n_heads, int n_blocks, int n_c);
+
+pf_status pf_score_select(const pf_bf16* q, int64_t n_q, int n_heads,
+                          const pf_bf16* pool_k, int n_blocks, int n_c, int top_k,
+                          int32_t* ids_out, float* scores_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * Placement of the selected blocks -> per-block temporal shift delta
+ * [PackForcing arXiv HTML, "The Position Misalignment Problem" and
+ *  "Incremental RoPE adjustment"; openbayes summary, "Method": the remaining
+ *  tokens are shifted to continuous indices]
+ *
+ * pos_tags[m] is the first latent frame that pool block m's keys currently
+ * encode. The selected blocks ids[0] < ... < ids[top_k-1] are laid end to end
+ * just before the recent block, whose first frame is recent_first_frame:
+ *   target_r   = recent_first_frame - (top_k - r) * block_frames
+ *   deltas[r]  = target_r - pos_tags[ids[r]]      (signed, latent frames)
+ *   pos_tags[ids[r]] = target_r                   (updated in place)
+ *
+ *   ids         int32[top_k] (device), ascending and distinct.
+ *   pos_tags    int32[n_blocks] (device), read and updated.
+ *   deltas_out  int32[top_k] (device).
+ * An id outside [0, n_blocks) gets delta 0 and leaves pos_tags untouched.
+ * Limits: 1 <= top_k <= PF_MAX_TOPK, top_k <= n_blocks, block_frames >= 1.
+ * ------------------------------------------------------------------------- */
+pf_status pf_selection_deltas(const int32_t* ids, int top_k, int32_t* pos_tags, int n_blocks,
+                              int32_t recent_first_frame, int32_t block_frames,
+                              int32_t* deltas_out, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * Incremental temporal RoPE shift, in place
+ * [PackForcing digest, 前置知识 RoPE (k^(p) = k_raw e^{i theta p}, and
+ *  e^{i theta p} e^{i theta delta} = e^{i theta (p+delta)}) and 方法步骤详情 (4);
+ *  arXiv HTML, "Incremental RoPE adjustment": k' = k e^{i(theta_t delta, 1_h, 1_w)}]
+ *
+ * For every row of each listed block and every head, the 22 temporal complex
+ * pairs (dims 2j, 2j+1 for j < 22) are multiplied by e^{+i theta_j delta} with
+ * theta_j = rope_base^(-2j/44); dims 44..127 are not touched, V is never
+ * touched, and a zero delta leaves the block's bits unchanged. The angle, its
+ * cos/sin and the rotation are fp64; the result is rounded once to bf16
+ * (round to nearest even).
+ *
+ *   k           [n_blocks*rows_per_block][n_heads][128] bf16, updated in place.
+ *   block_ids   int32[n_shift] (device) — blocks to shift; NULL means blocks
+ *               0..n_shift-1 (e.g. a contiguous sink slab as one block).
+ *   deltas      int32[n_shift] (device) — shift of each listed block, frames.
+ * Entries whose block id is outside [0, n_blocks) are skipped. A block listed
+ * twice is rotated twice (the order of the two rotations is unspecified).
+ * Limits: 1 <= n_heads <= PF_MAX_HEADS, rows_per_block >= 1, n_shift >= 0
+ *         (0 enqueues nothing), n_shift <= n_blocks when block_ids is NULL,
+ *         rope_base > 1.
+ * ------------------------------------------------------------------------- */
+pf_status pf_rope_shift(pf_bf16* k, int n_heads, int64_t rows_per_block, int64_t n_blocks,
+                        const int32_t* block_ids, const int32_t* deltas, int n_shift,
+                        double rope_base, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * Partition attention over the bounded context
+ * [PackForcing digest, 前置知识 KV缓存 (Attn(Q_i, C) = softmax(Q_i K^T / sqrt(d_h)) V)
+ *  and 方法步骤详情 (5); arXiv HTML, "Bounded Attention Context"]
+ *
+ *   O[i,h,:] = sum_t softmax_t(scale * Q[i,h,:] . K[t,h,:]) V[t,h,:]
+ * with one softmax over the virtual concatenation
+ *   K = sink || pool[mid_ids[0]] || ... || pool[mid_ids[n_sel-1]] || recent || cur
+ * (V follows the same row map). The selected pool blocks are read in place
+ * through mid_ids, never copied. There is no mask: the current block attends
+ * to itself in full.
+ *
+ *   q                    [n_q][n_heads][128] bf16.
+ *   sink_k/v  [n_sink]   recent_k/v [n_recent]   cur_k/v [n_cur] — row counts
+ *                        may be 0 (then the pointers may be NULL).
+ *   pool_k/v             [n_blocks*n_c][n_heads][128]; read only if n_sel > 0.
+ *   mid_ids              int32[n_sel] (device). An id outside [0, n_blocks)
+ *                        contributes no keys (its rows are masked out).
+ *   scale                softmax scale; <= 0 selects 1/sqrt(128).
+ *   o                    [n_q][n_heads][128] bf16 output (round to nearest even).
+ *   lse                  float[n_heads][n_q] natural-log sum-exp of the scaled
+ *                        scores, or NULL.
+ *   workspace            device scratch of pf_partition_attn_workspace_bytes(...)
+ *                        bytes (may be NULL when that is 0).
+ * Limits: 1 <= n_heads <= PF_MAX_HEADS, n_q >= 1, 0 <= n_sel <= PF_MAX_SELECTED,
+ *         n_sel <= n_blocks, the total key count must be >= 1 and < 2^31.
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; the online softmax is
+ * fp32; probabilities are rounded to bf16 before the P.V product.
+ * ------------------------------------------------------------------------- */
+size_t pf_partition_attn_workspace_bytes(int64_t n_q, int n_heads, int64_t n_keys);
+
+pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_heads,
+                            const pf_bf16* sink_k, const pf_bf16* sink_v, int64_t n_sink,
+                            const pf_bf16* pool_k, const pf_bf16* pool_v, int n_blocks, int n_c,
+                            const int32_t* mid_ids, int n_sel,
+                            const pf_bf16* recent_k, const pf_bf16* recent_v, int64_t n_recent,
+                            const pf_bf16* cur_k, const pf_bf16* cur_v, int64_t n_cur,
+                            float scale, pf_bf16* o, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PF_H_ */

@@ -152,10 +152,13 @@ def rope_shift_blocks(pool_k_bits: np.ndarray, n_c: int, block_ids: Sequence[int
     """Shift every row of each listed pool block by its delta; store as bf16.
 
     The pool is kept in bfloat16, so each shifted key is rounded back to bf16.
+    A zero delta is the identity rotation and leaves the stored bits alone.
     Returns a new bit array; V is never rotated.
     """
     out = np.array(pool_k_bits, dtype=np.uint16, copy=True)
     for b, d in zip(block_ids, deltas):
+        if int(d) == 0:
+            continue
         rows = slice(int(b) * n_c, (int(b) + 1) * n_c)
         k = bf16_to_f64(out[rows])
         out[rows, ..., :T_DIMS] = f64_to_bf16(rope_shift(k, float(d), base)[..., :T_DIMS])
@@ -247,18 +250,20 @@ def attn_bruteforce(q_bits: np.ndarray, k_parts: Sequence[np.ndarray], v_parts: 
 
     Returns O [n_q, H, D] and the natural-log LSE [H, n_q], in float64.
     """
-    q = bf16_to_f64(q_bits)
-    k = bf16_to_f64(np.concatenate(k_parts, axis=0))
-    v = bf16_to_f64(np.concatenate(v_parts, axis=0))
-    n_q, H, _ = q.shape
-    o = np.empty_like(q)
+    k_all = np.concatenate(k_parts, axis=0)
+    v_all = np.concatenate(v_parts, axis=0)
+    n_q, H, _ = q_bits.shape
+    o = np.empty((n_q, H, HEAD_DIM))
     lse = np.empty((H, n_q))
     for h in range(H):
-        s = (q[:, h, :] @ k[:, h, :].T) * scale          # [n_q, n_k]
+        q = bf16_to_f64(q_bits[:, h, :])
+        k = bf16_to_f64(k_all[:, h, :])
+        v = bf16_to_f64(v_all[:, h, :])
+        s = (q @ k.T) * scale                              # [n_q, n_k]
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
         z = e.sum(axis=1, keepdims=True)
-        o[:, h, :] = (e / z) @ v[:, h, :]
+        o[:, h, :] = (e / z) @ v
         lse[h] = (m + np.log(z))[:, 0]
     return o, lse
 
@@ -271,18 +276,18 @@ def attn_partitioned(q_bits: np.ndarray, k_parts: Sequence[np.ndarray], v_parts:
     U_p = sum exp(s - m_p) v. Then m = max_p m_p, l = sum_p e^{m_p - m} l_p and
     O = sum_p e^{m_p - m} U_p / l. Empty partitions are skipped.
     """
-    q = bf16_to_f64(q_bits)
-    n_q, H, D = q.shape
-    o = np.empty_like(q)
+    n_q, H, D = q_bits.shape
+    o = np.empty((n_q, H, D))
     lse = np.empty((H, n_q))
-    parts = [(bf16_to_f64(kp), bf16_to_f64(vp)) for kp, vp in zip(k_parts, v_parts) if kp.shape[0] > 0]
+    parts = [(kp, vp) for kp, vp in zip(k_parts, v_parts) if kp.shape[0] > 0]
     for h in range(H):
+        q = bf16_to_f64(q_bits[:, h, :])
         stats = []
-        for k, v in parts:
-            s = (q[:, h, :] @ k[:, h, :].T) * scale
+        for kp, vp in parts:
+            s = (q @ bf16_to_f64(kp[:, h, :]).T) * scale
             m_p = s.max(axis=1)
             e = np.exp(s - m_p[:, None])
-            stats.append((m_p, e.sum(axis=1), e @ v[:, h, :]))
+            stats.append((m_p, e.sum(axis=1), e @ bf16_to_f64(vp[:, h, :])))
         m = np.max(np.stack([st[0] for st in stats]), axis=0)
         l = np.zeros(n_q)
         u = np.zeros((n_q, D))

@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before anything reaches the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def pf():
+    import bounded_kv_cache_pf_amd as pf
+    return pf
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "pf.h")).read()
+    return sorted(set(re.findall(r"^[a-z_0-9 ]+\**\s*\**(pf_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_path():
+    names = _declared()
+    for n in ("pf_score_select", "pf_selection_deltas", "pf_rope_shift", "pf_partition_attn",
+              "pf_score_select_workspace_bytes", "pf_partition_attn_workspace_bytes", "pf_abi_version",
+              "pf_status_name", "pf_last_error_message"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(pf):
+    for n in _declared():
+        assert hasattr(pf.lib, n), n
+    assert pf.lib.pf_abi_version() == 1
+
+
+def test_status_names(pf):
+    assert pf.lib.pf_status_name(0) == b"PF_OK"
+    assert pf.lib.pf_status_name(6) == b"PF_ERR_WORKSPACE"
+    assert pf.lib.pf_status_name(99) == b"PF_UNKNOWN"
+
+
+A = 0x10000   # fake, aligned device addresses: validation fails before any use
+B = 0x20000
+C = 0x30000
+
+
+def _err(pf, st):
+    return pf.lib.pf_status_name(st).decode(), pf.lib.pf_last_error_message().decode()
+
+
+def test_score_select_validation(pf):
+    L = pf.lib
+    ws = L.pf_score_select_workspace_bytes(6240, 12, 40, 182)
+    assert ws > 40 * 182 // 64 * 4
+    assert L.pf_score_select_workspace_bytes(0, 12, 40, 182) == 0
+    assert _err(pf, L.pf_score_select(None, 6240, 12, B, 40, 182, 16, C, None, A, ws, None))[0] == "PF_ERR_NULL"
+    name, msg = _err(pf, L.pf_score_select(A, 6240, 12, B, 40, 182, 41, C, None, A, ws, None))
+    assert name == "PF_ERR_RANGE" and "top_k" in msg
+    assert _err(pf, L.pf_score_select(A, 6240, 12, B, 40, 182, 0, C, None, A, ws, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_score_select(A, 6240, 12, B, 40, 182, 257, C, None, A, ws, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_score_select(A, 6240, 33, B, 40, 182, 16, C, None, A, ws, None))[0] == "PF_ERR_UNSUPPORTED"
+    assert _err(pf, L.pf_score_select(A, 6240, 12, B, 5000, 182, 16, C, None, A, ws, None))[0] == "PF_ERR_UNSUPPORTED"
+    assert _err(pf, L.pf_score_select(A + 2, 6240, 12, B, 40, 182, 16, C, None, A, ws, None))[0] == "PF_ERR_MISALIGNED"
+    name, msg = _err(pf, L.pf_score_select(A, 6240, 12, B, 40, 182, 16, C, None, A, ws - 1, None))
+    assert name == "PF_ERR_WORKSPACE" and str(ws) in msg
+    assert _err(pf, L.pf_score_select(A, 6240, 12, B, 40, 182, 16, C, None, None, ws, None))[0] == "PF_ERR_WORKSPACE"
+    assert _err(pf, L.pf_score_select(A, 0, 12, B, 40, 182, 16, C, None, A, ws, None))[0] == "PF_ERR_SHAPE"
+
+
+def test_deltas_validation(pf):
+    L = pf.lib
+    assert _err(pf, L.pf_selection_deltas(None, 16, B, 40, 168, 4, C, None))[0] == "PF_ERR_NULL"
+    assert _err(pf, L.pf_selection_deltas(A, 41, B, 40, 168, 4, C, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_selection_deltas(A, 16, B, 40, 168, 0, C, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_selection_deltas(A + 1, 16, B, 40, 168, 4, C, None))[0] == "PF_ERR_MISALIGNED"
+
+
+def test_rope_validation(pf):
+    L = pf.lib
+    assert L.pf_rope_shift(None, 12, 182, 40, None, None, 0, 1e4, None) == 0     # nothing to do
+    assert L.pf_last_error_message() == b""
+    assert _err(pf, L.pf_rope_shift(None, 12, 182, 40, B, C, 16, 1e4, None))[0] == "PF_ERR_NULL"
+    assert _err(pf, L.pf_rope_shift(A, 12, 182, 40, B, None, 16, 1e4, None))[0] == "PF_ERR_NULL"
+    assert _err(pf, L.pf_rope_shift(A, 40, 182, 40, B, C, 16, 1e4, None))[0] == "PF_ERR_UNSUPPORTED"
+    assert _err(pf, L.pf_rope_shift(A, 12, 182, 40, None, C, 41, 1e4, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_rope_shift(A, 12, 182, 40, B, C, -1, 1e4, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_rope_shift(A, 12, 182, 40, B, C, 16, 1.0, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_rope_shift(A + 8, 12, 182, 40, B, C, 16, 1e4, None))[0] == "PF_ERR_MISALIGNED"
+    assert _err(pf, L.pf_rope_shift(A, 12, 0, 40, B, C, 16, 1e4, None))[0] == "PF_ERR_SHAPE"
+
+
+def _attn(pf, **kw):
+    args = dict(q=A, n_q=6240, H=12, sk=B, sv=C, ns=12480, pk=B, pv=C, nb=40, nc=182, ids=A, nsel=16,
+                rk=B, rv=C, nr=6240, ck=B, cv=C, ncur=6240, scale=0.0, o=A, lse=None, ws=None, wsb=0)
+    args.update(kw)
+    a = args
+    return pf.lib.pf_partition_attn(a["q"], a["n_q"], a["H"], a["sk"], a["sv"], a["ns"], a["pk"], a["pv"],
+                                    a["nb"], a["nc"], a["ids"], a["nsel"], a["rk"], a["rv"], a["nr"],
+                                    a["ck"], a["cv"], a["ncur"], a["scale"], a["o"], a["lse"], a["ws"],
+                                    a["wsb"], None)
+
+
+def test_attn_validation(pf):
+    assert _err(pf, _attn(pf, q=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, _attn(pf, o=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, _attn(pf, sk=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, _attn(pf, ids=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, _attn(pf, nsel=41))[0] == "PF_ERR_RANGE"
+    assert _err(pf, _attn(pf, nsel=1025, nb=2000))[0] == "PF_ERR_RANGE"
+    assert _err(pf, _attn(pf, H=0))[0] == "PF_ERR_UNSUPPORTED"
+    assert _err(pf, _attn(pf, n_q=0))[0] == "PF_ERR_SHAPE"
+    assert _err(pf, _attn(pf, nc=0))[0] == "PF_ERR_SHAPE"
+    assert _err(pf, _attn(pf, ns=-1))[0] == "PF_ERR_SHAPE"
+    assert _err(pf, _attn(pf, ns=0, nsel=0, nr=0, ncur=0))[0] == "PF_ERR_SHAPE"
+    assert _err(pf, _attn(pf, rk=B + 4))[0] == "PF_ERR_MISALIGNED"
+    assert _err(pf, _attn(pf, lse=A + 2))[0] == "PF_ERR_MISALIGNED"
+    assert _err(pf, _attn(pf, ns=1 << 31))[0] == "PF_ERR_UNSUPPORTED"
+    assert pf.lib.pf_partition_attn_workspace_bytes(6240, 12, 27872) == 0
+
+
+def test_binding_rejects_cpu_tensors(pf):
+    import torch
+    q = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pf.pf_partition_attn(q, q, q, None, None, 8, None, None, None, q, q)

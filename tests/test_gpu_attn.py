@@ -1,0 +1,135 @@
+"""GPU parity: pf_partition_attn against the oracle's softmax attention."""
+import numpy as np
+import pytest
+import torch
+
+import bounded_kv_cache_pf_amd as pf
+import oracle as O
+import pfgen
+from gpu_util import MAX_ABS, MEAN_ABS, REL_L2, attn_errors, dev, dev_i32, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(c, n_c, ids, want_lse=True, scale=0.0):
+    mid = dev_i32(ids) if len(ids) else None
+    o, lse = pf.pf_partition_attn(dev(c["q"]), dev(c["sink_k"]), dev(c["sink_v"]),
+                                  dev(c["pool_k"]) if len(ids) else None,
+                                  dev(c["pool_v"]) if len(ids) else None, n_c, mid,
+                                  dev(c["recent_k"]), dev(c["recent_v"]), dev(c["cur_k"]), dev(c["cur_v"]),
+                                  scale=scale, want_lse=want_lse)
+    torch.cuda.synchronize()
+    return host(o), (lse.cpu().numpy() if lse is not None else None)
+
+
+def _compare(c, n_c, ids, rows=None, label=""):
+    o, lse = _run(c, n_c, ids)
+    ks, vs = O.partitions(c, n_c, ids)
+    q = c["q"] if rows is None else c["q"][rows]
+    ref, ref_lse = O.attn_partitioned(q, ks, vs)
+    got = o if rows is None else o[rows]
+    got_lse = lse if rows is None else lse[:, rows]
+    mx, mean, rel = attn_errors(got, ref)
+    lse_err = float(np.max(np.abs(got_lse - ref_lse)))
+    say(f"  attn {label}: max-abs {mx:.3e} mean-abs {mean:.3e} rel-L2 {rel:.3e} lse {lse_err:.2e} "
+        f"(|O| rms {np.sqrt(np.mean(ref ** 2)):.3e})")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2
+    assert lse_err <= 1e-3
+    return o
+
+
+def _sample_rows(n_q, seed=0, extra=48):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, n_q // 2, n_q - 97, n_q - 96, n_q - 33, n_q - 32, n_q - 1]
+    rows = set(r for r in fixed if 0 <= r < n_q) | set(rng.integers(0, n_q, extra).tolist())
+    return np.array(sorted(rows))
+
+
+def test_attn_c0_all_rows():
+    say("test_attn_c0_all_rows")
+    cfg = pfgen.C0
+    for seed in (1000, 1001, 1002):
+        c = pfgen.make(cfg, seed)
+        ids = sorted(np.random.default_rng(seed).choice(cfg.pool_blocks, cfg.top_k, replace=False).tolist())
+        _compare(c, cfg.n_c, ids, label=f"C0 seed {seed}")
+
+
+@pytest.mark.parametrize("cfg", [pfgen.C1, pfgen.C2], ids=lambda c: c.name)
+def test_attn_full_size_sampled_rows(cfg):
+    say(f"test_attn_full_size_sampled_rows {cfg.name}")
+    c = pfgen.make(cfg)
+    ids = sorted(np.random.default_rng(cfg.seed).choice(cfg.pool_blocks, cfg.top_k, replace=False).tolist())
+    _compare(c, cfg.n_c, ids, rows=_sample_rows(cfg.n), label=cfg.name)
+
+
+def test_attn_sharp_scores():
+    # Q x 8: score std ~4, a peaked softmax that exercises the running-max rescale
+    say("test_attn_sharp_scores")
+    cfg = pfgen.C1.replace(q_mult=8.0)
+    c = pfgen.make(cfg)
+    ids = list(range(0, 40, 3))[:16]
+    _compare(c, cfg.n_c, ids, rows=_sample_rows(cfg.n, 1), label="C1 q*8")
+
+
+def test_attn_ragged_shapes_and_empty_partitions():
+    say("test_attn_ragged_shapes_and_empty_partitions")
+    rng = np.random.default_rng(7)
+
+    def bits(rows, H=3):
+        return O.f64_to_bf16(rng.standard_normal((rows, H, 128)))
+    base = dict(q=bits(200), sink_k=bits(77), sink_v=bits(77), pool_k=bits(9 * 13), pool_v=bits(9 * 13),
+                recent_k=bits(65), recent_v=bits(65), cur_k=bits(200), cur_v=bits(200))
+    _compare(base, 13, [8, 0, 4], label="ragged")                      # unsorted ids are fine
+    e = dict(base, sink_k=bits(0), sink_v=bits(0))
+    _compare(e, 13, [1, 2], label="no sink")
+    _compare(base, 13, [], label="no mid")
+    e = dict(base, sink_k=bits(0), sink_v=bits(0), recent_k=bits(0), recent_v=bits(0))
+    _compare(e, 13, [3], label="mid + cur only")
+    e = dict(base, q=bits(1), cur_k=bits(1), cur_v=bits(1), sink_k=bits(0), sink_v=bits(0),
+             recent_k=bits(0), recent_v=bits(0))
+    _compare(e, 13, [], label="one query, one key")
+
+
+def test_attn_zero_queries_mean_of_values():
+    say("test_attn_zero_queries_mean_of_values")
+    cfg = pfgen.C0
+    c = pfgen.make(cfg)
+    c["q"] = np.zeros_like(c["q"])
+    ids = [0, 2, 4, 6]
+    o, lse = _run(c, cfg.n_c, ids)
+    ks, vs = O.partitions(c, cfg.n_c, ids)
+    mean_v = O.bf16_to_f64(np.concatenate(vs)).mean(axis=0)
+    assert np.max(np.abs(O.bf16_to_f64(o) - mean_v[None])) < 1e-3
+    assert np.max(np.abs(lse - np.log(1056))) < 1e-4
+
+
+def test_attn_invalid_ids_are_masked():
+    say("test_attn_invalid_ids_are_masked")
+    cfg = pfgen.C0
+    c = pfgen.make(cfg)
+    o_bad, _ = _run(c, cfg.n_c, [1, -5, 3, 99])
+    ks, vs = O.partitions(c, cfg.n_c, [1, 3])
+    ref, _ = O.attn_partitioned(c["q"], ks, vs)
+    mx, mean, rel = attn_errors(o_bad, ref)
+    assert mx <= MAX_ABS and rel <= REL_L2
+
+
+def test_attn_gather_equals_copy():
+    # reading the pool through ids == attending over the copied rows as a partition
+    say("test_attn_gather_equals_copy")
+    cfg = pfgen.C0
+    c = pfgen.make(cfg)
+    ids = [7, 2, 5, 9]
+    o1, _ = _run(c, cfg.n_c, ids)
+    mid_k = O.gather_mid(c["pool_k"], cfg.n_c, ids)
+    mid_v = O.gather_mid(c["pool_v"], cfg.n_c, ids)
+    c2 = dict(c, sink_k=np.concatenate([c["sink_k"], mid_k]), sink_v=np.concatenate([c["sink_v"], mid_v]))
+    o2, _ = _run(c2, cfg.n_c, [])
+    assert np.array_equal(o1, o2)
+
+
+def test_attn_unbounded_c4_sampled_rows():
+    say("test_attn_unbounded_c4_sampled_rows (generating 748,800 keys)")
+    cfg = pfgen.C4
+    c = pfgen.make(cfg)
+    _compare(c, cfg.n_c, [], rows=_sample_rows(cfg.n, 4, extra=8), label="C4 748,800 keys")

@@ -1,0 +1,122 @@
+"""GPU parity: pf_score_select and pf_selection_deltas against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import bounded_kv_cache_pf_amd as pf
+import oracle as O
+import pfgen
+from gpu_util import dev, dev_i32, say
+
+pytestmark = pytest.mark.gpu
+
+FLAG_GAP = 1e-3
+
+
+def _select(c, n_c, k):
+    ids, scores = pf.pf_score_select(dev(c["q"]), dev(c["pool_k"]), n_c, k)
+    return ids.cpu().numpy().tolist(), scores.cpu().numpy().astype(np.float64)
+
+
+def _compare(c, n_c, k, require_unflagged=False):
+    ref_s = O.block_scores(c["q"], c["pool_k"], n_c)
+    ref_ids = O.select_topk(ref_s, k)
+    gap = O.topk_gap(ref_s, k)
+    ids, s = _select(c, n_c, k)
+    err = float(np.max(np.abs(s - ref_s)))
+    flagged = gap < FLAG_GAP
+    say(f"  select: M={len(ref_s)} k={k} score max-abs err {err:.2e}, spread {np.ptp(ref_s):.3e}, "
+        f"k/k+1 gap {gap:.3e}{' FLAGGED' if flagged else ''}")
+    assert err <= 1e-5 + 1e-5 * float(np.max(np.abs(ref_s)))
+    assert ids == sorted(ids) and len(set(ids)) == k
+    if require_unflagged:
+        assert not flagged
+    if flagged:
+        assert O.topk_acceptable(ids, ref_s, k, FLAG_GAP)
+    else:
+        assert ids == ref_ids
+    return ids, flagged
+
+
+@pytest.mark.parametrize("cfg", [pfgen.C0, pfgen.C1, pfgen.C2, pfgen.C2Q], ids=lambda c: c.name)
+def test_select_configs(cfg):
+    say(f"test_select_configs {cfg.name}")
+    for seed in (cfg.seed, cfg.seed + 1, cfg.seed + 2):
+        _compare(pfgen.make(cfg, seed), cfg.n_c, cfg.top_k)
+
+
+def test_select_planted_answer_full_size():
+    say("test_select_planted_answer_full_size")
+    cfg = pfgen.C2
+    chosen = [0, 9, 17, 30, 41, 42, 43, 57, 60, 71, 88, 90, 99, 100, 114, 115]
+    c = pfgen.planted_pool(cfg, 77, chosen, margin=4.0)
+    ids, _ = _compare(c, cfg.n_c, 16, require_unflagged=True)
+    assert ids == chosen
+
+
+def test_select_ties_go_to_lower_index():
+    say("test_select_ties_go_to_lower_index")
+    cfg = pfgen.C1
+    c = pfgen.make(cfg)
+    s = O.block_scores(c["q"], c["pool_k"], cfg.n_c)
+    order = np.argsort(-s, kind="stable")
+    kth = int(order[15])                     # the last block that makes the top 16
+    dup = 39 if kth != 39 else 38
+    n = cfg.n_c
+    pk = c["pool_k"].copy()
+    pk[dup * n:(dup + 1) * n] = pk[kth * n:(kth + 1) * n]
+    c2 = dict(c, pool_k=pk)
+    ids, scores = _select(c2, n, 16)
+    assert scores[dup] == scores[kth]          # identical blocks, identical fp32 scores
+    ref = O.select_topk(O.block_scores(c2["q"], pk, n), 16)
+    assert ids == ref
+    assert min(kth, dup) in ids and max(kth, dup) not in ids
+
+
+def test_select_k_equals_m_and_limits():
+    say("test_select_k_equals_m_and_limits")
+    cfg = pfgen.C0
+    c = pfgen.make(cfg)
+    ids, _ = _select(c, cfg.n_c, cfg.pool_blocks)
+    assert ids == list(range(cfg.pool_blocks))
+    # the largest pool and top-k the library accepts (tiny blocks keep it fast)
+    rng = np.random.default_rng(21)
+    q = O.f64_to_bf16(rng.standard_normal((300, 2, 128)) + rng.standard_normal((1, 2, 128)))
+    pk = O.f64_to_bf16(rng.standard_normal((4096 * 2, 2, 128)) + np.repeat(rng.standard_normal((4096, 1, 2, 128)), 2, axis=1).reshape(-1, 2, 128))
+    _compare({"q": q, "pool_k": pk}, 2, 256)
+    _compare({"q": q, "pool_k": pk[:2 * 1000]}, 2, 1)
+
+
+def test_select_repeatable_bits():
+    say("test_select_repeatable_bits")
+    cfg = pfgen.C1
+    c = pfgen.make(cfg)
+    q, pk = dev(c["q"]), dev(c["pool_k"])
+    a = pf.pf_score_select(q, pk, cfg.n_c, 16)[1].cpu().numpy()
+    b = pf.pf_score_select(q, pk, cfg.n_c, 16)[1].cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg", [pfgen.C1, pfgen.C2], ids=lambda c: c.name)
+def test_deltas_match_oracle_over_steps(cfg):
+    say(f"test_deltas_match_oracle_over_steps {cfg.name}")
+    M, k, Bf = cfg.pool_blocks, cfg.top_k, cfg.block_frames
+    tags = O.initial_pos_tags(M, cfg.sink_blocks, Bf)
+    tags_dev = dev_i32(tags)
+    Fr = (cfg.sink_blocks + M) * Bf
+    rng = np.random.default_rng(cfg.seed)
+    for step in range(5):
+        ids = sorted(rng.choice(M, k, replace=False).tolist())
+        d_ref, tags = O.placement_deltas(ids, tags, Fr, Bf)
+        d = pf.pf_selection_deltas(dev_i32(ids), tags_dev, Fr, Bf)
+        assert d.cpu().numpy().tolist() == d_ref.tolist()
+        assert tags_dev.cpu().numpy().tolist() == tags.tolist()
+
+
+def test_deltas_invalid_ids():
+    say("test_deltas_invalid_ids")
+    tags = dev_i32([8, 12, 4, 20])
+    d = pf.pf_selection_deltas(dev_i32([-3, 2, 9]), tags, 24, 4)
+    # r = 1: target 24 - (3 - 1) * 4 = 16, delta 16 - 4; out-of-range ids get 0
+    assert d.cpu().numpy().tolist() == [0, 12, 0]
+    assert tags.cpu().numpy().tolist() == [8, 12, 16, 20]
