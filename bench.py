@@ -1,0 +1,217 @@
+"""Benchmark of one layer-step of PackForcing's per-block context attention on
+one MI355X.
+
+A step is the whole path on the default single-layer workload (6,240 queries,
+12 heads, 27,872 keys = 12,480 sink + 16 x 182 selected from a 40-block pool
++ 6,240 recent + 6,240 current):
+  pf_score_select -> pf_selection_deltas -> pf_rope_shift -> pf_partition_attn
+Each step moves the recent block one block forward in time (as the next
+generated block does), so every selected block gets a non-zero shift.
+
+Prints one JSON line. `value` is partition-attention TFLOP/s over the whole
+step (4 n_q n_k 128 H flops per step / step time); the per-kernel times,
+the attention kernel's roofline and the CPU oracle's rate are alongside.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (the 2.5 PFLOP/s figure)
+PEAK_HBM_GBS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "partition_attn_c1_hbm_counters.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def attn_flops(n_q, n_k, heads):
+    return 4.0 * n_q * n_k * 128 * heads
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "bounded_kv_cache_pf_amd", "csrc", "pf_attn.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters():
+    """HBM bytes per attention launch from the committed counter summary, if it
+    was taken on the current kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cache, cfg, seconds):
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    tags = O.initial_pos_tags(cfg.pool_blocks, cfg.sink_blocks, cfg.block_frames)
+    fr = (cfg.sink_blocks + cfg.pool_blocks) * cfg.block_frames
+    t0 = time.perf_counter()
+    O.layer_step(cache, tags, cfg.n_c, cfg.top_k, fr, cfg.block_frames, q_rows=np.arange(256))
+    t_cal = time.perf_counter() - t0
+    rows = int(min(cfg.n, max(256, 256 * seconds / max(t_cal, 1e-3))))
+    rows = (rows // 64) * 64
+    t0 = time.perf_counter()
+    O.layer_step(cache, tags, cfg.n_c, cfg.top_k, fr, cfg.block_frames, q_rows=np.arange(rows))
+    dt = time.perf_counter() - t0
+    tflops = attn_flops(rows, cfg.n_keys, cfg.heads) / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the fp64 numpy oracle's full layer-step (scoring of all 6,240 queries and the "
+                      f"40-block pool, placement, RoPE shift, and attention for the first {rows} of 6,240 "
+                      f"query rows over all 27,872 keys), {dt:.1f} s wall; value = attention flops of the "
+                      f"sample / wall time",
+            "seconds": dt, "rows": rows}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is single-GPU by design "
+              "and runs on one MI355X.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    import bounded_kv_cache_pf_amd as pf
+    import pfgen
+
+    cfg = pfgen.C1
+    t_gen = time.perf_counter()
+    cache = pfgen.make(cfg)
+    t_gen = time.perf_counter() - t_gen
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    t = {k: dev(v) for k, v in cache.items()}
+    M, k, Bf = cfg.pool_blocks, cfg.top_k, cfg.block_frames
+    # pool block m starts out encoding frames from (sink blocks + m) * B_f on
+    tags = torch.tensor((cfg.sink_blocks + np.arange(M)) * Bf, dtype=torch.int32, device="cuda")
+    ids = torch.empty(k, dtype=torch.int32, device="cuda")
+    scores = torch.empty(M, dtype=torch.float32, device="cuda")
+    deltas = torch.empty(k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(pf.pf_score_select_workspace_bytes(cfg.n, cfg.heads, M, cfg.n_c), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(t["q"])
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        fr = (cfg.sink_blocks + M + i) * Bf
+        if ev: ev[0].record(stream)
+        pf.pf_score_select(t["q"], t["pool_k"], cfg.n_c, k, ids_out=ids, scores_out=scores, workspace=ws)
+        if ev: ev[1].record(stream)
+        pf.pf_selection_deltas(ids, tags, fr, Bf, deltas_out=deltas)
+        if ev: ev[2].record(stream)
+        pf.pf_rope_shift(t["pool_k"], cfg.n_c, deltas, ids)
+        if ev: ev[3].record(stream)
+        pf.pf_partition_attn(t["q"], t["sink_k"], t["sink_v"], t["pool_k"], t["pool_v"], cfg.n_c, ids,
+                             t["recent_k"], t["recent_v"], t["cur_k"], t["cur_v"], o=o)
+        if ev: ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    part = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])   # [steps, 4] ms
+    ms_select, ms_deltas, ms_rope, ms_attn = part.mean(axis=0)
+
+    flops = attn_flops(cfg.n, cfg.n_keys, cfg.heads)
+    value = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (ms_attn * 1e-3) / 1e12
+    # algorithmic bytes: Q + K,V of every context key + O (bf16)
+    row_bytes = cfg.heads * 128 * 2
+    attn_bytes = row_bytes * (2 * cfg.n + 2 * cfg.n_keys)
+    sel_bytes = row_bytes * (cfg.n + M * cfg.n_c)
+    rope_bytes = 2 * k * cfg.n_c * cfg.heads * 88
+
+    out = {
+        "metric": "partition-attention TFLOP/s and ms/layer-step at 27,872 keys; % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(2) bf16 caches of the pages' default shapes)",
+        "config": {"workload": "default single layer-step: 6,240 queries x 12 heads x 128 over 27,872 keys "
+                               "(12,480 sink + 16 of 40 compressed 182-token blocks + 6,240 recent + "
+                               "6,240 current); select -> place -> RoPE shift -> attend",
+                   "n_q": cfg.n, "n_keys": cfg.n_keys, "heads": cfg.heads, "pool_blocks": M, "top_k": k,
+                   "n_c": cfg.n_c},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_counters(),
+                     "kernel": "partition_attn_kernel", "flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": attn_bytes},
+        "kernels_ms": {"score_select": round(float(ms_select), 5), "selection_deltas": round(float(ms_deltas), 5),
+                       "rope_shift": round(float(ms_rope), 5), "partition_attn": round(float(ms_attn), 5)},
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_frac_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "score_select_gbs": round(sel_bytes / (ms_select * 1e-3) / 1e9, 1),
+        "rope_shift_gbs": round(rope_bytes / (ms_rope * 1e-3) / 1e9, 1),
+        "input_gen_s": round(t_gen, 2),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cache, cfg, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

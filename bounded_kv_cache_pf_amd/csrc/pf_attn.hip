@@ -7,19 +7,30 @@
 // list; nothing is concatenated in memory.
 //
 // Design (gfx950, wave64, bf16 MFMA 32x32x16 with fp32 accumulation):
-//  * A workgroup of 4 waves owns 128 queries of one head; each wave owns 32.
-//  * Keys stream in tiles of 64 through LDS (double-buffered, loaded with
-//    16-byte global loads, rows resolved per partition). K and V stay row-major
-//    in LDS; the PV product reads V with the gfx950 transposing LDS read.
+//  * A workgroup of 4 waves owns a unit = 128 queries of one head; each wave
+//    owns 32 queries. Two workgroups share a CU (occupancy 2), so one wave's
+//    softmax overlaps the other wave's matrix products on the same SIMD.
+//  * Keys stream in tiles of 64 straight from global memory into LDS
+//    (global_load_lds, 16 bytes per lane, no register staging), double
+//    buffered. Each 256-byte LDS row holds one key's 128 dims with its 16-byte
+//    chunks XOR-swizzled by the row, so the K reads (16 bytes per lane) and the
+//    transposing V reads (8 bytes per lane) hit distinct banks.
 //  * The score tile is computed transposed, S^T = K Q^T, so each lane holds one
-//    query's scores in registers: row max / row sum are per-lane (plus one swap
-//    between the two half-waves for the max), and the probabilities are already
-//    in the B-operand layout of O^T = V^T P^T.
-//  * Online softmax in the log2 domain (scale * log2 e folded into one FMA).
-//  * Workgroups are numbered so that each XCD (workgroup id mod 8) walks a
-//    contiguous range of (head, query tile) pairs: tiles that share K/V share
-//    that XCD's L2.
+//    query's 32 scores: the row max needs one swap between half-waves, the row
+//    sum none, and the probabilities are already in the B-operand layout of
+//    O^T = V^T P^T. V is read with the gfx950 transposing LDS read.
+//  * Online softmax in the log2 domain. The running max is only raised when a
+//    tile's max exceeds it by more than 2^8, so the O rescale (a wave-uniform
+//    branch) runs on a handful of tiles; exp2 arguments stay <= 8 in between.
+//  * Scheduling: with G resident workgroups and U units, the first
+//    floor(U/G) rounds give every workgroup whole units, numbered so that each
+//    XCD walks consecutive units of one head in lockstep (shared K/V in its
+//    L2). The remaining units are cut into equal runs of key tiles; runs that
+//    cover part of a unit write unnormalised partial results that a small
+//    merge kernel combines. This removes the tail round of idle CUs.
 #include <math.h>
+
+#include <mutex>
 
 #include "pf_internal.h"
 
@@ -32,11 +43,14 @@ using pf::short4v;
 constexpr int D = PF_HEAD_DIM;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = kWaves * 32;       // queries per workgroup
-constexpr int kBN = 64;                // keys per tile
-constexpr int kStride = D + 16;        // LDS row stride in bf16 (288 bytes): conflict-free reads
-constexpr int kTileElems = kBN * kStride;
+constexpr int kBM = kWaves * 32;         // queries per unit
+constexpr int kBN = 64;                  // keys per tile
+constexpr int kOcc = 2;                  // workgroups per CU the kernel is built for
 constexpr int kXcds = 8;
+constexpr float kRescaleSlack = 8.0f;    // log2 units: p may grow to 2^8 before a rescale
+constexpr int kMinTailTiles = 16;        // shortest run of key tiles worth a partial
+constexpr size_t kPartFloats = static_cast<size_t>(kBM) * D + 2 * kBM;   // U, m, l
+constexpr size_t kPartBytes = kPartFloats * 4;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -50,22 +64,30 @@ struct AttnArgs {
   const uint16_t* v_rec;
   const uint16_t* k_cur;
   const uint16_t* v_cur;
+  const uint16_t* k_safe;   // a row that exists, loaded for masked keys
+  const uint16_t* v_safe;
   const int32_t* mid_ids;
+  float* part;              // partial results of split units (workspace)
   int64_t n_q;
+  int64_t row_stride;       // H * 128
   int32_t H;
   int32_t n_c;
   int32_t n_sel;
   int32_t n_blocks;
   int32_t e_sink, e_mid, e_rec, e_cur;   // cumulative ends of the partitions (e_cur = key count)
   int32_t num_qtiles;
-  int32_t total_tiles;
+  int32_t units;            // num_qtiles * H
+  int32_t n_kt;             // key tiles per unit
+  int32_t G;                // workgroups in the grid
+  int32_t rounds;           // rounds of whole units
+  int32_t n_tail;           // units split into runs (after the whole rounds)
+  int32_t n_chunks;         // runs the split units are cut into (0: none)
+  int64_t tail_tiles;       // n_tail * n_kt
   float scale_log2;
 };
 
-// Source row of virtual key kk for head h; returns false for keys that do not
-// exist (past the end, or inside a mid block whose id is out of range).
 __device__ __forceinline__ bool resolve_key(const AttnArgs& a, const int32_t* ids_lds, int32_t kk,
-                                            const uint16_t*& kp, const uint16_t*& vp, int64_t& off) {
+                                            const uint16_t*& kp, const uint16_t*& vp) {
   int64_t row;
   if (kk < a.e_sink) {
     kp = a.k_sink; vp = a.v_sink; row = kk;
@@ -73,57 +95,45 @@ __device__ __forceinline__ bool resolve_key(const AttnArgs& a, const int32_t* id
     const int32_t x = kk - a.e_sink;
     const int32_t b = x / a.n_c;
     const int32_t id = ids_lds[b];
-    if (id < 0 || id >= a.n_blocks) return false;
+    if (id < 0 || id >= a.n_blocks) {
+      kp = a.k_safe; vp = a.v_safe;
+      return false;
+    }
     kp = a.k_pool; vp = a.v_pool; row = static_cast<int64_t>(id) * a.n_c + (x - b * a.n_c);
   } else if (kk < a.e_rec) {
     kp = a.k_rec; vp = a.v_rec; row = kk - a.e_mid;
   } else if (kk < a.e_cur) {
     kp = a.k_cur; vp = a.v_cur; row = kk - a.e_rec;
   } else {
+    kp = a.k_safe; vp = a.v_safe;
     return false;
   }
-  off = row * a.H * D;
+  kp += row * a.row_stride;
+  vp += row * a.row_stride;
   return true;
 }
 
-struct TileRegs {
-  uint4 k[4];
-  uint4 v[4];
-  bool valid[4];
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Thread t moves 16-byte chunk (t & 15) of tile rows (t >> 4) + 16 i, i < 4.
-__device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* ids_lds, int h, int32_t k0,
-                                          TileRegs& r) {
-  const int t = threadIdx.x;
-  const int col = (t & 15) * 8;
+// Issue the loads of key tile kt (keys kt*64 ..) into LDS buffers ks/vs.
+// Wave w fills rows 16w .. 16w+15, four rows (1 KB) per instruction; lane L
+// lands on row 16w + 4i + L/16, physical chunk L%16, which holds logical
+// chunk (L%16) ^ swz(row), swz(row) = 2 (row & 7).
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, const int32_t* ids_lds, int h, int32_t kt,
+                                           uint16_t* ks, uint16_t* vs, uint8_t* kbad, int wave_u, int lane) {
+  const int pchunk = lane & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = (t >> 4) + 16 * i;
+    const int row = 16 * wave_u + 4 * i + (lane >> 4);
     const uint16_t* kp;
     const uint16_t* vp;
-    int64_t off;
-    r.valid[i] = resolve_key(a, ids_lds, k0 + row, kp, vp, off);
-    if (r.valid[i]) {
-      off += static_cast<int64_t>(h) * D + col;
-      r.k[i] = *reinterpret_cast<const uint4*>(kp + off);
-      r.v[i] = *reinterpret_cast<const uint4*>(vp + off);
-    } else {
-      r.k[i] = make_uint4(0, 0, 0, 0);
-      r.v[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint16_t* vs, uint8_t* kbad) {
-  const int t = threadIdx.x;
-  const int col = (t & 15) * 8;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (t >> 4) + 16 * i;
-    *reinterpret_cast<uint4*>(ks + row * kStride + col) = r.k[i];
-    *reinterpret_cast<uint4*>(vs + row * kStride + col) = r.v[i];
-    if ((t & 15) == 0) kbad[row] = r.valid[i] ? 0 : 1;
+    const bool ok = resolve_key(a, ids_lds, kt * kBN + row, kp, vp);
+    const int lchunk = pchunk ^ ((row & 7) << 1);
+    const int off = h * D + lchunk * 8;
+    const int lds_row = 16 * wave_u + 4 * i;
+    __builtin_amdgcn_global_load_lds(kp + off, (lds_void*)(ks + lds_row * D), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp + off, (lds_void*)(vs + lds_row * D), 16, 0, 0);
+    if (pchunk == 0) kbad[row] = ok ? 0 : 1;
   }
 }
 
@@ -137,52 +147,36 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
 __device__ __forceinline__ short4v lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
 }
 
-__global__ __launch_bounds__(kThreads, 1) void partition_attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kTileElems];
-  __shared__ uint8_t kbad[2][kBN];
-  __shared__ int32_t ids_lds[PF_MAX_SELECTED];
-  __shared__ int any_bad_id;
+struct Smem {
+  uint16_t ks[2][kBN * D];
+  uint16_t vs[2][kBN * D];
+  uint8_t kbad[2][kBN];
+  int32_t ids[PF_MAX_SELECTED];
+  int any_bad_id;
+};
 
-  // XCD-aware numbering: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of logical tiles (head-major, then query tile).
-  const int b = blockIdx.x;
-  const int per = a.total_tiles / kXcds, rem = a.total_tiles % kXcds;
-  const int xcd = b % kXcds, slot = b / kXcds;
-  const int logical = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-  const int h = logical / a.num_qtiles;
-  const int64_t q0 = static_cast<int64_t>(logical % a.num_qtiles) * kBM;
-
+// One unit (head h, queries q0 .. q0+127) over key tiles [kt0, kt1).
+// direct: the run covers the whole unit -> write O (and LSE); otherwise write
+// the unnormalised partial U, m (log2 domain) and l to partial slot `slot`.
+__device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int64_t q0, int kt0, int kt1,
+                                         bool direct, int64_t slot) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int g = lane >> 5;      // half-wave
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  if (tid == 0) any_bad_id = 0;
-  __syncthreads();
-  for (int i = tid; i < a.n_sel; i += kThreads) {
-    const int32_t id = a.mid_ids[i];
-    ids_lds[i] = id;
-    if (id < 0 || id >= a.n_blocks) any_bad_id = 1;
-  }
-  __syncthreads();
-  const bool bad_ids = any_bad_id != 0;
-
-  // Q^T operand: lane holds query (q0 + 32 wave + l32), dims 16 st + 8 g .. +7.
+  // Q^T operand: query q0 + 32 wave + l32, dims 16 st + 8 g .. +7.
   const int64_t qrow = q0 + wave * 32 + l32;
   const bool qvalid = qrow < a.n_q;
   bf16x8 qf[8];
   {
-    const uint16_t* qp = a.q + (qvalid ? qrow : 0) * a.H * D + static_cast<int64_t>(h) * D + 8 * g;
+    const uint16_t* qp = a.q + (qvalid ? qrow : 0) * a.row_stride + static_cast<int64_t>(h) * D + 8 * g;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * st);
@@ -197,71 +191,87 @@ __global__ __launch_bounds__(kThreads, 1) void partition_attn_kernel(AttnArgs a)
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  const int32_t n_keys = a.e_cur;
-  const int n_tiles = (n_keys + kBN - 1) / kBN;
+  // Per-lane LDS offsets (elements). K: row kb*32 + l32, logical chunk 2st + g
+  // sits at physical chunk 2(st ^ (l32 & 7)) + g.
+  const int k_sw = l32 & 7;
+  const int k_base = l32 * D + 8 * g;
+  // V: row 16c + 4g + (lane&15)/4 (+8), logical elements 32db + 16dh + 4(lane&3).
+  const int v_r = 4 * g + ((lane & 15) >> 2);
+  const int v_sw = (v_r & 7) << 1;
+  const int v_dh = (lane >> 4) & 1;
+  const int v_u = (lane & 3) >> 1;
+  const int v_h = lane & 1;
+  int v_off[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) v_off[db] = v_r * D + (((4 * db + 2 * v_dh + v_u) ^ v_sw) << 3) + 4 * v_h;
 
-  TileRegs regs;
-  load_tile(a, ids_lds, h, 0, regs);
-  store_tile(regs, ks[0], vs[0], kbad[0]);
+  issue_tile(a, sm.ids, h, kt0, sm.ks[0], sm.vs[0], sm.kbad[0], wave_u, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    const int32_t k0 = it * kBN;
-    const bool has_next = it + 1 < n_tiles;
-    if (has_next) load_tile(a, ids_lds, h, k0 + kBN, regs);
+  const bool bad_ids = sm.any_bad_id != 0;
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    const int32_t k0 = kt * kBN;
+    if (kt + 1 < kt1)
+      issue_tile(a, sm.ids, h, kt + 1, sm.ks[buf ^ 1], sm.vs[buf ^ 1], sm.kbad[buf ^ 1], wave_u, lane);
 
-    const uint16_t* kt = ks[buf];
-    const uint16_t* vt = vs[buf];
+    const uint16_t* kt_lds = sm.ks[buf];
+    const uint16_t* vt_lds = sm.vs[buf];
 
     // ---- S^T = K Q^T for two 32-key blocks ----
     floatx16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = floatx16{};
-      const uint16_t* kr = kt + (kb * 32 + l32) * kStride + 8 * g;
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kr + 16 * st), qf[st], s[kb], 0, 0, 0);
+      for (int st = 0; st < 8; ++st) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt_lds + kb * 32 * D + k_base + 16 * (st ^ k_sw));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[kb], 0, 0, 0);
+      }
     }
 
     // ---- mask keys that do not exist ----
-    const bool need_mask = (k0 + kBN > n_keys) || (bad_ids && k0 < a.e_mid && k0 + kBN > a.e_sink);
+    const bool need_mask = (k0 + kBN > a.e_cur) || (bad_ids && k0 < a.e_mid && k0 + kBN > a.e_sink);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (kbad[buf][key]) s[kb][i] = -INFINITY;
+          if (sm.kbad[buf][key]) s[kb][i] = -INFINITY;
         }
     }
 
-    // ---- online softmax (log2 domain) ----
-    float mx = -INFINITY;
+    // ---- online softmax (log2 domain, lazy rescale) ----
+    float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    mx = half_swap_max(mx) * a.scale_log2;
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(fmaf(s[kb][i], a.scale_log2, -m_use));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_use));
         s[kb][i] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    l_run += psum;
 
     // ---- P^T as the B operand: chunk c covers keys 16c .. 16c+15 ----
     bf16x8 pb[4];
@@ -271,45 +281,208 @@ __global__ __launch_bounds__(kThreads, 1) void partition_attn_kernel(AttnArgs a)
       for (int t = 0; t < 8; ++t) pb[c][t] = static_cast<__bf16>(s[c >> 1][8 * (c & 1) + t]);
 
     // ---- O^T += V^T P^T ----
-    // Transposing read: lane (row 16c + 4g + (lane&15)/4, col 32db + 16((lane>>4)&1) + 4(lane&3))
-    // delivers dims 32db + l32 for keys 16c + 4g + 0..3 (and +8 for the second read).
-    const int vrow = 4 * g + ((lane & 15) >> 2);
-    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint16_t* vp = vt + (16 * c + vrow) * kStride + 32 * db + vcol;
+        const uint16_t* vp = vt_lds + 16 * c * D + v_off[db];
         const short4v lo = lds_read_tr(vp);
-        const short4v hi = lds_read_tr(vp + 8 * kStride);
+        const short4v hi = lds_read_tr(vp + 8 * D);
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], acc[db], 0, 0, 0);
       }
     }
 
-    if (has_next) store_tile(regs, ks[buf ^ 1], vs[buf ^ 1], kbad[buf ^ 1]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
-  // ---- epilogue ----
   const float l_tot = half_swap_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qvalid) {
-    uint16_t* op = a.o + qrow * a.H * D + static_cast<int64_t>(h) * D;
+  if (direct) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qvalid) {
+      uint16_t* op = a.o + qrow * a.row_stride + static_cast<int64_t>(h) * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int dim = 32 * db + 8 * qd + 4 * g;
+          uint2 w;
+          w.x = pf::pack_bf16x2(acc[db][4 * qd + 0] * inv, acc[db][4 * qd + 1] * inv);
+          w.y = pf::pack_bf16x2(acc[db][4 * qd + 2] * inv, acc[db][4 * qd + 3] * inv);
+          *reinterpret_cast<uint2*>(op + dim) = w;
+        }
+      // log2 of l by the hardware log (v_log_f32 is base 2); LSE in natural log
+      if (a.lse != nullptr && g == 0)
+        a.lse[static_cast<int64_t>(h) * a.n_q + qrow] =
+            l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
+  } else {
+    // partial slot: U [128 queries][128 dims], then m [128], l [128]
+    float* base = a.part + slot * static_cast<int64_t>(kPartFloats);
+    const int ql = wave * 32 + l32;
+    float* up = base + static_cast<int64_t>(ql) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const int dim = 32 * db + 8 * qd + 4 * g;
-        uint2 w;
-        w.x = pf::pack_bf16x2(acc[db][4 * qd + 0] * inv, acc[db][4 * qd + 1] * inv);
-        w.y = pf::pack_bf16x2(acc[db][4 * qd + 2] * inv, acc[db][4 * qd + 3] * inv);
-        *reinterpret_cast<uint2*>(op + dim) = w;
+        *reinterpret_cast<float4*>(up + dim) =
+            make_float4(acc[db][4 * qd + 0], acc[db][4 * qd + 1], acc[db][4 * qd + 2], acc[db][4 * qd + 3]);
       }
-    if (a.lse != nullptr && g == 0)
-      a.lse[static_cast<int64_t>(h) * a.n_q + qrow] =
-          l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    if (g == 0) {
+      base[kBM * D + ql] = m_run;
+      base[kBM * D + kBM + ql] = l_tot;
+    }
   }
+}
+
+// Workgroup g runs on XCD g % 8; XCD x gets the consecutive slots x*G/8 .. .
+__device__ __forceinline__ int xcd_slot(int g, int G) {
+  return (G % kXcds == 0) ? (g % kXcds) * (G / kXcds) + g / kXcds : g;
+}
+
+__global__ __launch_bounds__(kThreads, kOcc) void partition_attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+  const int tid = threadIdx.x;
+  if (tid == 0) sm.any_bad_id = 0;
+  __syncthreads();
+  for (int i = tid; i < a.n_sel; i += kThreads) {
+    const int32_t id = a.mid_ids[i];
+    sm.ids[i] = id;
+    if (id < 0 || id >= a.n_blocks) sm.any_bad_id = 1;
+  }
+  __syncthreads();
+
+  const int slot = xcd_slot(blockIdx.x, a.G);
+  for (int r = 0; r < a.rounds; ++r) {
+    const int unit = r * a.G + slot;
+    if (unit >= a.units) break;
+    run_unit(a, sm, unit / a.num_qtiles, static_cast<int64_t>(unit % a.num_qtiles) * kBM, 0, a.n_kt, true, 0);
+  }
+  if (slot < a.n_chunks) {
+    const int64_t b = static_cast<int64_t>(slot) * a.tail_tiles / a.n_chunks;
+    const int64_t e = static_cast<int64_t>(slot + 1) * a.tail_tiles / a.n_chunks;
+    for (int64_t it = b; it < e;) {
+      const int64_t tu = it / a.n_kt;                 // split unit index
+      const int64_t u_end = (tu + 1) * a.n_kt;
+      const int64_t seg_end = e < u_end ? e : u_end;
+      const int kt0 = static_cast<int>(it - tu * a.n_kt);
+      const int kt1 = static_cast<int>(seg_end - tu * a.n_kt);
+      const int unit = a.units - a.n_tail + static_cast<int>(tu);
+      const bool whole = kt0 == 0 && kt1 == a.n_kt;
+      run_unit(a, sm, unit / a.num_qtiles, static_cast<int64_t>(unit % a.num_qtiles) * kBM, kt0, kt1, whole,
+               slot + tu);
+      it = seg_end;
+    }
+  }
+}
+
+// Merge the partial runs of split units: one workgroup per split unit. Run c
+// covers key tiles [c*T/C, (c+1)*T/C) of the split units' tile sequence, so the
+// run holding tile t is ((t+1)*C - 1) / T.
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+  const int tu = blockIdx.x;
+  const int64_t first = static_cast<int64_t>(tu) * a.n_kt;
+  const int64_t last = first + a.n_kt - 1;
+  const int c0 = static_cast<int>(((first + 1) * a.n_chunks - 1) / a.tail_tiles);
+  const int c1 = static_cast<int>(((last + 1) * a.n_chunks - 1) / a.tail_tiles);
+  if (c0 == c1) return;   // one run covered the unit and wrote O directly
+  const int unit = a.units - a.n_tail + tu;
+  const int h = unit / a.num_qtiles;
+  const int64_t q0 = static_cast<int64_t>(unit % a.num_qtiles) * kBM;
+  // thread t: query t/2, dims (t&1)*64 .. +63
+  const int ql = threadIdx.x >> 1;
+  const int d0 = (threadIdx.x & 1) * 64;
+  const int64_t qrow = q0 + ql;
+  float m = -INFINITY;
+  for (int c = c0; c <= c1; ++c) m = fmaxf(m, a.part[(c + tu) * static_cast<int64_t>(kPartFloats) + kBM * D + ql]);
+  const float m_use = m == -INFINITY ? 0.f : m;
+  float l = 0.f;
+  float u[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) u[i] = 0.f;
+  for (int c = c0; c <= c1; ++c) {
+    const float* base = a.part + (c + tu) * static_cast<int64_t>(kPartFloats);
+    const float w = __builtin_amdgcn_exp2f(base[kBM * D + ql] - m_use);
+    l += w * base[kBM * D + kBM + ql];
+    const float* up = base + static_cast<int64_t>(ql) * D + d0;
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(up + i);
+      u[i] += w * v.x;
+      u[i + 1] += w * v.y;
+      u[i + 2] += w * v.z;
+      u[i + 3] += w * v.w;
+    }
+  }
+  if (qrow >= a.n_q) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* op = a.o + qrow * a.row_stride + static_cast<int64_t>(h) * D + d0;
+#pragma unroll
+  for (int i = 0; i < 64; i += 8) {
+    uint4 w;
+    w.x = pf::pack_bf16x2(u[i] * inv, u[i + 1] * inv);
+    w.y = pf::pack_bf16x2(u[i + 2] * inv, u[i + 3] * inv);
+    w.z = pf::pack_bf16x2(u[i + 4] * inv, u[i + 5] * inv);
+    w.w = pf::pack_bf16x2(u[i + 6] * inv, u[i + 7] * inv);
+    *reinterpret_cast<uint4*>(op + i) = w;
+  }
+  if (a.lse != nullptr && d0 == 0)
+    a.lse[static_cast<int64_t>(h) * a.n_q + qrow] =
+        l > 0.f ? (m_use + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+}
+
+// ---- launch plan ----
+
+struct Plan {
+  int64_t units = 0, n_kt = 0;
+  int grid = 0, G = 0, rounds = 0, n_tail = 0, n_chunks = 0;
+  int64_t tail_tiles = 0;
+  size_t ws_bytes = 0;
+};
+
+int resident_workgroups() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, partition_attn_kernel, kThreads, 0) != hipSuccess ||
+        per <= 0)
+      per = 1;
+    cached[dev] = cus * per;
+  }
+  return cached[dev];
+}
+
+// rounds of whole units first; a remainder under 3/4 of the machine is cut
+// into runs of key tiles (at least kMinTailTiles each), otherwise it runs as
+// one more round of whole units.
+Plan make_plan(int64_t n_q, int H, int64_t n_keys, int resident) {
+  Plan p;
+  p.units = ((n_q + kBM - 1) / kBM) * H;
+  p.n_kt = (n_keys + kBN - 1) / kBN;
+  const int64_t full = p.units / resident;
+  const int64_t rem = p.units - full * resident;
+  p.rounds = static_cast<int>(full);
+  if (rem > 0 && (rem * 4 < static_cast<int64_t>(resident) * 3 || full == 0)) {
+    p.n_tail = static_cast<int>(rem);
+    p.tail_tiles = rem * p.n_kt;
+    int64_t c = p.tail_tiles / kMinTailTiles;
+    if (c > resident) c = resident;
+    if (c < rem) c = rem;
+    p.n_chunks = static_cast<int>(c);
+    p.ws_bytes = static_cast<size_t>(p.n_chunks + p.n_tail) * kPartBytes;
+  } else if (rem > 0) {
+    p.rounds += 1;
+  }
+  p.grid = full > 0 ? resident : p.n_chunks;
+  p.G = p.grid;
+  return p;
 }
 
 bool is_aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -317,10 +490,8 @@ bool is_aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) =
 }  // namespace
 
 extern "C" size_t pf_partition_attn_workspace_bytes(int64_t n_q, int n_heads, int64_t n_keys) {
-  (void)n_q;
-  (void)n_heads;
-  (void)n_keys;
-  return 0;
+  if (n_q < 1 || n_heads < 1 || n_heads > PF_MAX_HEADS || n_keys < 1) return 0;
+  return make_plan(n_q, n_heads, n_keys, resident_workgroups()).ws_bytes;
 }
 
 extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* sink_k,
@@ -330,8 +501,6 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
                                        int64_t n_recent, const pf_bf16* cur_k, const pf_bf16* cur_v, int64_t n_cur,
                                        float scale, pf_bf16* o, float* lse, void* workspace,
                                        size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   PF_REQUIRE_PTR(q);
   PF_REQUIRE_PTR(o);
   PF_REQUIRE_ALIGNED(q);
@@ -378,8 +547,15 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
   PF_REQUIRE(n_keys < (int64_t{1} << 31) - kBN, PF_ERR_UNSUPPORTED, "too many keys (%lld)",
              static_cast<long long>(n_keys));
   const int64_t num_qtiles = (n_q + kBM - 1) / kBM;
-  const int64_t total = num_qtiles * n_heads;
-  PF_REQUIRE(total < 0x7FFFFFFF, PF_ERR_UNSUPPORTED, "too many query tiles");
+  PF_REQUIRE(num_qtiles * n_heads < 0x7FFFFFFF, PF_ERR_UNSUPPORTED, "too many query tiles");
+
+  const Plan p = make_plan(n_q, n_heads, n_keys, resident_workgroups());
+  if (p.ws_bytes > 0) {
+    PF_REQUIRE(workspace != nullptr, PF_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", p.ws_bytes);
+    PF_REQUIRE(workspace_bytes >= p.ws_bytes, PF_ERR_WORKSPACE, "workspace has %zu bytes, need %zu",
+               workspace_bytes, p.ws_bytes);
+    PF_REQUIRE_ALIGNED(workspace);
+  }
 
   AttnArgs a{};
   a.q = reinterpret_cast<const uint16_t*>(q);
@@ -393,8 +569,20 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
   a.v_rec = reinterpret_cast<const uint16_t*>(recent_v);
   a.k_cur = reinterpret_cast<const uint16_t*>(cur_k);
   a.v_cur = reinterpret_cast<const uint16_t*>(cur_v);
+  // masked keys load a row that exists (their scores are discarded)
+  if (n_sink > 0) {
+    a.k_safe = a.k_sink; a.v_safe = a.v_sink;
+  } else if (n_recent > 0) {
+    a.k_safe = a.k_rec; a.v_safe = a.v_rec;
+  } else if (n_cur > 0) {
+    a.k_safe = a.k_cur; a.v_safe = a.v_cur;
+  } else {
+    a.k_safe = a.k_pool; a.v_safe = a.v_pool;
+  }
   a.mid_ids = mid_ids;
+  a.part = static_cast<float*>(workspace);
   a.n_q = n_q;
+  a.row_stride = static_cast<int64_t>(n_heads) * D;
   a.H = n_heads;
   a.n_c = n_sel > 0 ? n_c : 1;
   a.n_sel = n_sel;
@@ -404,10 +592,20 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
   a.e_rec = static_cast<int32_t>(n_sink + n_mid + n_recent);
   a.e_cur = static_cast<int32_t>(n_keys);
   a.num_qtiles = static_cast<int32_t>(num_qtiles);
-  a.total_tiles = static_cast<int32_t>(total);
+  a.units = static_cast<int32_t>(p.units);
+  a.n_kt = static_cast<int32_t>(p.n_kt);
+  a.G = p.G;
+  a.rounds = p.rounds;
+  a.n_tail = p.n_tail;
+  a.n_chunks = p.n_chunks;
+  a.tail_tiles = p.tail_tiles;
   const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(D));
   a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
-  hipLaunchKernelGGL(partition_attn_kernel, dim3(static_cast<unsigned>(total)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return pf::launch_status("pf_partition_attn");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(partition_attn_kernel, dim3(p.grid), dim3(kThreads), 0, st, a);
+  pf_status s = pf::launch_status("pf_partition_attn");
+  if (s != PF_OK || p.n_chunks == 0) return s;
+  hipLaunchKernelGGL(merge_kernel, dim3(p.n_tail), dim3(256), 0, st, a);
+  return pf::launch_status("pf_partition_attn (merge)");
 }

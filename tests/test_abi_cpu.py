@@ -116,7 +116,12 @@ def test_attn_validation(pf):
     assert _err(pf, _attn(pf, rk=B + 4))[0] == "PF_ERR_MISALIGNED"
     assert _err(pf, _attn(pf, lse=A + 2))[0] == "PF_ERR_MISALIGNED"
     assert _err(pf, _attn(pf, ns=1 << 31))[0] == "PF_ERR_UNSUPPORTED"
-    assert pf.lib.pf_partition_attn_workspace_bytes(6240, 12, 27872) == 0
+    need = pf.lib.pf_partition_attn_workspace_bytes(6240, 12, 27872)
+    assert need > 0
+    name, msg = _err(pf, _attn(pf, ws=None, wsb=0))
+    assert name == "PF_ERR_WORKSPACE" and str(need) in msg
+    assert _err(pf, _attn(pf, ws=C, wsb=need - 1))[0] == "PF_ERR_WORKSPACE"
+    assert _err(pf, _attn(pf, ws=C + 8, wsb=need))[0] == "PF_ERR_MISALIGNED"
 
 
 def test_binding_rejects_cpu_tensors(pf):

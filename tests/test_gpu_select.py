@@ -61,7 +61,7 @@ def test_select_ties_go_to_lower_index():
     s = O.block_scores(c["q"], c["pool_k"], cfg.n_c)
     order = np.argsort(-s, kind="stable")
     kth = int(order[15])                     # the last block that makes the top 16
-    dup = 39 if kth != 39 else 38
+    dup = int(order[-1])                     # the lowest-ranked block, outside the top 16
     n = cfg.n_c
     pk = c["pool_k"].copy()
     pk[dup * n:(dup + 1) * n] = pk[kth * n:(kth + 1) * n]
