@@ -14,7 +14,9 @@
 //    (global_load_lds, 16 bytes per lane, no register staging), double
 //    buffered. Each 256-byte LDS row holds one key's 128 dims with its 16-byte
 //    chunks XOR-swizzled by the row, so the K reads (16 bytes per lane) and the
-//    transposing V reads (8 bytes per lane) hit distinct banks.
+//    transposing V reads (8 bytes per lane) hit distinct banks. Tiles inside a
+//    contiguous partition take a uniform fast path; tiles in the mid blocks or
+//    at the end resolve each row.
 //  * The score tile is computed transposed, S^T = K Q^T, so each lane holds one
 //    query's 32 scores: the row max needs one swap between half-waves, the row
 //    sum none, and the probabilities are already in the B-operand layout of
@@ -115,21 +117,52 @@ __device__ __forceinline__ bool resolve_key(const AttnArgs& a, const int32_t* id
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// LDS row r stores its 16-byte chunk j at position j ^ swz(r). swz is a
+// bijection of r mod 16, so 16 consecutive rows read at one logical chunk hit
+// 16 distinct chunks (the K reads), and the 4-row x 4-chunk footprint of a
+// transposing V read lands on 16 distinct chunks as well.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // Issue the loads of key tile kt (keys kt*64 ..) into LDS buffers ks/vs.
 // Wave w fills rows 16w .. 16w+15, four rows (1 KB) per instruction; lane L
-// lands on row 16w + 4i + L/16, physical chunk L%16, which holds logical
-// chunk (L%16) ^ swz(row), swz(row) = 2 (row & 7).
+// lands on row 16w + 4i + L/16 at physical chunk L%16, so it fetches logical
+// chunk (L%16) ^ swz(row). lane_off[i] holds that lane's element offset within
+// a contiguous partition: (L/16) rows plus the logical chunk.
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const int32_t* ids_lds, int h, int32_t kt,
-                                           uint16_t* ks, uint16_t* vs, uint8_t* kbad, int wave_u, int lane) {
+                                           uint16_t* ks, uint16_t* vs, uint8_t* kbad, int wave_u, int lane,
+                                           const int* lane_off) {
+  const int32_t k0 = kt * kBN;
+  // fast path: the whole tile lies inside one contiguous partition (uniform)
+  const uint16_t* kbase = nullptr;
+  const uint16_t* vbase = nullptr;
+  int32_t r0 = 0;
+  if (k0 + kBN <= a.e_sink) {
+    kbase = a.k_sink; vbase = a.v_sink; r0 = k0;
+  } else if (k0 >= a.e_mid && k0 + kBN <= a.e_rec) {
+    kbase = a.k_rec; vbase = a.v_rec; r0 = k0 - a.e_mid;
+  } else if (k0 >= a.e_rec && k0 + kBN <= a.e_cur) {
+    kbase = a.k_cur; vbase = a.v_cur; r0 = k0 - a.e_rec;
+  }
+  if (kbase != nullptr) {
+    const int64_t off0 = (static_cast<int64_t>(r0) + 16 * wave_u) * a.row_stride + h * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = off0 + 4 * i * a.row_stride;
+      const int lds_row = 16 * wave_u + 4 * i;
+      __builtin_amdgcn_global_load_lds(kbase + off + lane_off[i], (lds_void*)(ks + lds_row * D), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + off + lane_off[i], (lds_void*)(vs + lds_row * D), 16, 0, 0);
+    }
+    return;
+  }
+  // general path: resolve each row (mid blocks through the ids, masked rows)
   const int pchunk = lane & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 16 * wave_u + 4 * i + (lane >> 4);
     const uint16_t* kp;
     const uint16_t* vp;
-    const bool ok = resolve_key(a, ids_lds, kt * kBN + row, kp, vp);
-    const int lchunk = pchunk ^ ((row & 7) << 1);
-    const int off = h * D + lchunk * 8;
+    const bool ok = resolve_key(a, ids_lds, k0 + row, kp, vp);
+    const int off = h * D + ((pchunk ^ swz(row)) << 3);
     const int lds_row = 16 * wave_u + 4 * i;
     __builtin_amdgcn_global_load_lds(kp + off, (lds_void*)(ks + lds_row * D), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(vp + off, (lds_void*)(vs + lds_row * D), 16, 0, 0);
@@ -191,21 +224,29 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // Per-lane LDS offsets (elements). K: row kb*32 + l32, logical chunk 2st + g
-  // sits at physical chunk 2(st ^ (l32 & 7)) + g.
-  const int k_sw = l32 & 7;
-  const int k_base = l32 * D + 8 * g;
-  // V: row 16c + 4g + (lane&15)/4 (+8), logical elements 32db + 16dh + 4(lane&3).
-  const int v_r = 4 * g + ((lane & 15) >> 2);
-  const int v_sw = (v_r & 7) << 1;
-  const int v_dh = (lane >> 4) & 1;
-  const int v_u = (lane & 3) >> 1;
-  const int v_h = lane & 1;
-  int v_off[4];
+  // Per-lane LDS offsets (elements), loop invariant.
+  // K (A operand of S^T): row kb*32 + l32, logical chunk 2st + g.
+  int k_off[8];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) v_off[db] = v_r * D + (((4 * db + 2 * v_dh + v_u) ^ v_sw) << 3) + 4 * v_h;
+  for (int st = 0; st < 8; ++st) k_off[st] = l32 * D + (((2 * st + g) ^ swz(l32)) << 3);
+  // V (transposing read): row 16c + 4g + (lane&15)/4 (+8 for the second read),
+  // logical elements 32db + 16dh + 4(lane&3) = chunk 4db + 2dh + (lane&3)/2, half lane&1.
+  const int v_r = 4 * g + ((lane & 15) >> 2);
+  const int v_x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int v_h = 4 * (lane & 1);
+  int v_lo[4], v_hi[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    v_lo[db] = v_r * D + (((4 * db + v_x) ^ swz(v_r)) << 3) + v_h;
+    v_hi[db] = (v_r + 8) * D + (((4 * db + v_x) ^ swz(v_r + 8)) << 3) + v_h;
+  }
+  // tile loader: element offset of this lane inside a contiguous partition
+  int lane_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    lane_off[i] = static_cast<int>((lane >> 4) * a.row_stride) + (((lane & 15) ^ swz(4 * i + (lane >> 4))) << 3);
 
-  issue_tile(a, sm.ids, h, kt0, sm.ks[0], sm.vs[0], sm.kbad[0], wave_u, lane);
+  issue_tile(a, sm.ids, h, kt0, sm.ks[0], sm.vs[0], sm.kbad[0], wave_u, lane, lane_off);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -214,7 +255,8 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
     const int buf = (kt - kt0) & 1;
     const int32_t k0 = kt * kBN;
     if (kt + 1 < kt1)
-      issue_tile(a, sm.ids, h, kt + 1, sm.ks[buf ^ 1], sm.vs[buf ^ 1], sm.kbad[buf ^ 1], wave_u, lane);
+      issue_tile(a, sm.ids, h, kt + 1, sm.ks[buf ^ 1], sm.vs[buf ^ 1], sm.kbad[buf ^ 1], wave_u, lane,
+                 lane_off);
 
     const uint16_t* kt_lds = sm.ks[buf];
     const uint16_t* vt_lds = sm.vs[buf];
@@ -226,7 +268,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
       s[kb] = floatx16{};
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt_lds + kb * 32 * D + k_base + 16 * (st ^ k_sw));
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt_lds + kb * 32 * D + k_off[st]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[kb], 0, 0, 0);
       }
     }
@@ -285,9 +327,8 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint16_t* vp = vt_lds + 16 * c * D + v_off[db];
-        const short4v lo = lds_read_tr(vp);
-        const short4v hi = lds_read_tr(vp + 8 * D);
+        const short4v lo = lds_read_tr(vt_lds + 16 * c * D + v_lo[db]);
+        const short4v hi = lds_read_tr(vt_lds + 16 * c * D + v_hi[db]);
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], acc[db], 0, 0, 0);
       }
