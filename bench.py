@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (the 2.5 PFLOP/s figure)
 PEAK_HBM_GBS = 8000.0
-PMC_FILE = os.path.join(ROOT, "profiles", "partition_attn_c1_hbm_counters.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "partition_attn_default_hbm_counters.json")
 
 
 def parse():
@@ -69,6 +69,9 @@ def traffic_from_counters():
 
 
 def cpu_baseline(cache, cfg, seconds):
+    """The oracle's layer-step on the host: whole steps repeated until about
+    `seconds` of wall time, or, if one whole step would take far longer, the
+    step restricted to its first query rows."""
     import oracle as O
     from threadpoolctl import threadpool_info
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -77,18 +80,28 @@ def cpu_baseline(cache, cfg, seconds):
     t0 = time.perf_counter()
     O.layer_step(cache, tags, cfg.n_c, cfg.top_k, fr, cfg.block_frames, q_rows=np.arange(256))
     t_cal = time.perf_counter() - t0
-    rows = int(min(cfg.n, max(256, 256 * seconds / max(t_cal, 1e-3))))
-    rows = (rows // 64) * 64
-    t0 = time.perf_counter()
-    O.layer_step(cache, tags, cfg.n_c, cfg.top_k, fr, cfg.block_frames, q_rows=np.arange(rows))
-    dt = time.perf_counter() - t0
-    tflops = attn_flops(rows, cfg.n_keys, cfg.heads) / dt / 1e12
+    est_full = t_cal * cfg.n / 256
+    if est_full > 2 * seconds:          # one whole step is too long: sample query rows
+        rows = max(256, (int(cfg.n * seconds / est_full) // 64) * 64)
+        t0 = time.perf_counter()
+        O.layer_step(cache, tags, cfg.n_c, cfg.top_k, fr, cfg.block_frames, q_rows=np.arange(rows))
+        dt = time.perf_counter() - t0
+        n_steps, what = 1, f"one layer-step restricted to the first {rows} of {cfg.n} query rows"
+    else:
+        rows, n_steps, dt = cfg.n, 0, 0.0
+        while dt < seconds:
+            t0 = time.perf_counter()
+            O.layer_step(cache, tags, cfg.n_c, cfg.top_k, fr, cfg.block_frames)
+            dt += time.perf_counter() - t0
+            n_steps += 1
+        what = f"{n_steps} whole layer-step(s) (all {cfg.n} query rows)"
+    tflops = n_steps * attn_flops(rows, cfg.n_keys, cfg.heads) / dt / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the fp64 numpy oracle's full layer-step (scoring of all 6,240 queries and the "
-                      f"40-block pool, placement, RoPE shift, and attention for the first {rows} of 6,240 "
-                      f"query rows over all 27,872 keys), {dt:.1f} s wall; value = attention flops of the "
-                      f"sample / wall time",
-            "seconds": dt, "rows": rows}
+            "sample": f"the fp64 numpy oracle on the bench workload: {what} -- scoring of all queries over "
+                      f"the {cfg.pool_blocks}-block pool, top-{cfg.top_k} selection, placement, RoPE shift "
+                      f"and attention over all {cfg.n_keys} keys; {dt:.1f} s wall; value = attention flops "
+                      f"of the sample / wall time",
+            "seconds": round(dt, 2), "rows": rows, "layer_steps": n_steps}
 
 
 def copy_calibration():
