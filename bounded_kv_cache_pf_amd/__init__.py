@@ -36,6 +36,11 @@ _SIGNATURES = {
     "pf_score_select": ([_p, _i64, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _sz, _p], _i32),
     "pf_selection_deltas": ([_p, _i32, _p, _i32, ctypes.c_int32, ctypes.c_int32, _p, _p], _i32),
     "pf_rope_shift": ([_p, _i32, _i64, _i64, _p, _p, _i32, ctypes.c_double, _p], _i32),
+    "pf_score_select_batched_workspace_bytes": ([_i64, _i32, _i32, _i32, _i32], _sz),
+    "pf_score_select_batched": ([_p, _i64, _i64, _i32, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _sz, _p],
+                                _i32),
+    "pf_selection_deltas_batched": ([_p, _i32, _p, _i32, ctypes.c_int32, ctypes.c_int32, _i32, _p, _p], _i32),
+    "pf_rope_shift_batched": ([_p, _i64, _i32, _i64, _i64, _p, _p, _i32, _i32, ctypes.c_double, _p], _i32),
     "pf_partition_attn_workspace_bytes": ([_i64, _i32, _i64], _sz),
     "pf_partition_attn": ([_p, _i64, _i32,
                            _p, _p, _i64,
@@ -159,6 +164,88 @@ def pf_rope_shift(k, rows_per_block: int, deltas, block_ids=None, rope_base: flo
         raise ValueError("block_ids and deltas differ in length")
     _check(lib.pf_rope_shift(_ptr(k), heads, rows_per_block, rows // rows_per_block, _ptr(block_ids),
                              _ptr(deltas), n_shift, rope_base, _stream(stream)), "pf_rope_shift")
+    return k
+
+
+def _batched_rows(t, what: str) -> Tuple[int, int, int, int]:
+    """(batch, rows, heads, batch stride in elements) of a [batch][rows][heads][128]
+    bf16 tensor whose caches are each contiguous (the batch stride may be larger
+    than one cache, e.g. a view of the first rows of bigger slabs)."""
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16):
+        raise TypeError(f"{what} must be bfloat16 (or int16 bf16 bits), got {t.dtype}")
+    if t.dim() != 4 or t.shape[3] != HEAD_DIM or not t[0].is_contiguous() or \
+            t.stride()[1:] != (t.shape[2] * HEAD_DIM, HEAD_DIM, 1):
+        raise ValueError(f"{what} must be [batch][rows][heads][128] with contiguous caches, got {tuple(t.shape)}")
+    return int(t.shape[0]), int(t.shape[1]), int(t.shape[2]), int(t.stride(0))
+
+
+def pf_score_select_batched_workspace_bytes(n_q: int, n_heads: int, n_blocks: int, n_c: int, n_batch: int) -> int:
+    return int(lib.pf_score_select_batched_workspace_bytes(n_q, n_heads, n_blocks, n_c, n_batch))
+
+
+def pf_score_select_batched(q, pool_k, n_c: int, top_k: int, ids_out=None, scores_out=None, workspace=None,
+                            stream=None):
+    """Selection over a batch of caches: q [B][n_q][H][128], pool_k [B][M*n_c][H][128].
+    Returns (ids int32[B][top_k], scores f32[B][M])."""
+    torch = _torch()
+    nb, n_q, heads, q_stride = _batched_rows(q, "q")
+    nb2, rows, heads2, p_stride = _batched_rows(pool_k, "pool_k")
+    if nb2 != nb or heads2 != heads:
+        raise ValueError("q and pool_k differ in batch or heads")
+    if n_c <= 0 or rows % n_c:
+        raise ValueError("pool rows must be a multiple of n_c")
+    n_blocks = rows // n_c
+    if ids_out is None:
+        ids_out = torch.empty((nb, top_k), dtype=torch.int32, device=q.device)
+    if scores_out is None:
+        scores_out = torch.empty((nb, n_blocks), dtype=torch.float32, device=q.device)
+    _i32_vec(ids_out, "ids_out")
+    need = pf_score_select_batched_workspace_bytes(n_q, heads, n_blocks, n_c, nb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.pf_score_select_batched(_ptr(q), q_stride, n_q, heads, _ptr(pool_k), p_stride, n_blocks, n_c,
+                                       top_k, nb, _ptr(ids_out), _ptr(scores_out), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)),
+           "pf_score_select_batched")
+    return ids_out, scores_out
+
+
+def pf_selection_deltas_batched(ids, pos_tags, recent_first_frame: int, block_frames: int, deltas_out=None,
+                                stream=None):
+    """Placement for a batch: ids int32[B][top_k], pos_tags int32[B][n_blocks] (updated)."""
+    torch = _torch()
+    _i32_vec(ids, "ids")
+    _i32_vec(pos_tags, "pos_tags")
+    if ids.dim() != 2 or pos_tags.dim() != 2 or ids.shape[0] != pos_tags.shape[0]:
+        raise ValueError("ids and pos_tags must be [batch][top_k] and [batch][n_blocks]")
+    if deltas_out is None:
+        deltas_out = torch.empty_like(ids)
+    _i32_vec(deltas_out, "deltas_out")
+    _check(lib.pf_selection_deltas_batched(_ptr(ids), int(ids.shape[1]), _ptr(pos_tags), int(pos_tags.shape[1]),
+                                           recent_first_frame, block_frames, int(ids.shape[0]), _ptr(deltas_out),
+                                           _stream(stream)), "pf_selection_deltas_batched")
+    return deltas_out
+
+
+def pf_rope_shift_batched(k, rows_per_block: int, deltas, block_ids=None, rope_base: float = 10000.0,
+                          stream=None):
+    """In-place temporal shift over a batch: k [B][rows][H][128], deltas int32[B][n_shift]."""
+    nb, rows, heads, k_stride = _batched_rows(k, "k")
+    if rows_per_block <= 0 or rows % rows_per_block:
+        raise ValueError("k rows must be a multiple of rows_per_block")
+    _i32_vec(deltas, "deltas")
+    _i32_vec(block_ids, "block_ids")
+    if deltas.dim() != 2 or deltas.shape[0] != nb:
+        raise ValueError("deltas must be [batch][n_shift]")
+    n_shift = int(deltas.shape[1])
+    if block_ids is not None and tuple(block_ids.shape) != tuple(deltas.shape):
+        raise ValueError("block_ids and deltas differ in shape")
+    _check(lib.pf_rope_shift_batched(_ptr(k), k_stride, heads, rows_per_block, rows // rows_per_block,
+                                     _ptr(block_ids), _ptr(deltas), n_shift, nb, rope_base, _stream(stream)),
+           "pf_rope_shift_batched")
     return k
 
 

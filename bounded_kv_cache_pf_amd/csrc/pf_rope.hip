@@ -48,10 +48,10 @@ __device__ __forceinline__ void rotate_pair(uint32_t& packed, double c, double s
 }
 
 __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
-    uint16_t* __restrict__ k, int64_t row_heads_per_block, int64_t n_blocks,
-    const int32_t* __restrict__ block_ids, const int32_t* __restrict__ deltas, double base) {
-  const int entry = blockIdx.y;
-  const int64_t blk = block_ids ? static_cast<int64_t>(block_ids[entry]) : entry;
+    uint16_t* __restrict__ k, int64_t k_bstride, int64_t row_heads_per_block, int64_t n_blocks,
+    const int32_t* __restrict__ block_ids, const int32_t* __restrict__ deltas, int n_shift, double base) {
+  const int64_t entry = static_cast<int64_t>(blockIdx.z) * n_shift + blockIdx.y;
+  const int64_t blk = block_ids ? static_cast<int64_t>(block_ids[entry]) : blockIdx.y;
   const int delta = deltas[entry];
   if (blk < 0 || blk >= n_blocks || delta == 0) return;   // delta 0 is the identity
 
@@ -65,43 +65,66 @@ __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
   const int sub = threadIdx.x % kLanesPerRowHead;
   const int local = threadIdx.x / kLanesPerRowHead;
   if (sub > 5) return;
-  uint16_t* blk_base = k + blk * row_heads_per_block * PF_HEAD_DIM;
+  uint16_t* blk_base = k + blockIdx.z * k_bstride + blk * row_heads_per_block * PF_HEAD_DIM;
+  const int64_t rh0 = static_cast<int64_t>(blockIdx.x) * kRowHeadsPerBlock + local;
+  // all loads first (kPasses row-heads in flight per lane), then rotate and store
+  uint4 w[kPasses];
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
-    const int64_t rh = static_cast<int64_t>(blockIdx.x) * kRowHeadsPerBlock + pass * kRowHeadsPerPass + local;
+    const int64_t rh = rh0 + pass * kRowHeadsPerPass;
+    w[pass] = make_uint4(0, 0, 0, 0);
+    if (rh < row_heads_per_block) {
+      const uint16_t* p = blk_base + rh * PF_HEAD_DIM + sub * 8;
+      if (sub < 5) {
+        w[pass] = *reinterpret_cast<const uint4*>(p);
+      } else {
+        const uint2 h = *reinterpret_cast<const uint2*>(p);
+        w[pass].x = h.x;
+        w[pass].y = h.y;
+      }
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int64_t rh = rh0 + pass * kRowHeadsPerPass;
     if (rh >= row_heads_per_block) break;
     uint16_t* p = blk_base + rh * PF_HEAD_DIM + sub * 8;
     if (sub < 5) {
-      uint4 w = *reinterpret_cast<uint4*>(p);
       const int j = sub * 4;
-      rotate_pair(w.x, cs[j + 0], sn[j + 0]);
-      rotate_pair(w.y, cs[j + 1], sn[j + 1]);
-      rotate_pair(w.z, cs[j + 2], sn[j + 2]);
-      rotate_pair(w.w, cs[j + 3], sn[j + 3]);
-      *reinterpret_cast<uint4*>(p) = w;
+      rotate_pair(w[pass].x, cs[j + 0], sn[j + 0]);
+      rotate_pair(w[pass].y, cs[j + 1], sn[j + 1]);
+      rotate_pair(w[pass].z, cs[j + 2], sn[j + 2]);
+      rotate_pair(w[pass].w, cs[j + 3], sn[j + 3]);
+      *reinterpret_cast<uint4*>(p) = w[pass];
     } else {
-      uint2 w = *reinterpret_cast<uint2*>(p);
-      rotate_pair(w.x, cs[20], sn[20]);
-      rotate_pair(w.y, cs[21], sn[21]);
-      *reinterpret_cast<uint2*>(p) = w;
+      rotate_pair(w[pass].x, cs[20], sn[20]);
+      rotate_pair(w[pass].y, cs[21], sn[21]);
+      *reinterpret_cast<uint2*>(p) = make_uint2(w[pass].x, w[pass].y);
     }
   }
 }
 
 }  // namespace
 
-extern "C" pf_status pf_rope_shift(pf_bf16* k, int n_heads, int64_t rows_per_block, int64_t n_blocks,
-                                   const int32_t* block_ids, const int32_t* deltas, int n_shift,
-                                   double rope_base, void* stream) {
+extern "C" pf_status pf_rope_shift_batched(pf_bf16* k, int64_t k_batch_stride, int n_heads, int64_t rows_per_block,
+                                           int64_t n_blocks, const int32_t* block_ids, const int32_t* deltas,
+                                           int n_shift, int n_batch, double rope_base, void* stream) {
   PF_REQUIRE(n_shift >= 0, PF_ERR_RANGE, "n_shift must be >= 0 (got %d)", n_shift);
   PF_REQUIRE(n_heads >= 1 && n_heads <= PF_MAX_HEADS, PF_ERR_UNSUPPORTED,
              "n_heads must be in [1, %d] (got %d)", PF_MAX_HEADS, n_heads);
   PF_REQUIRE(rows_per_block >= 1, PF_ERR_SHAPE, "rows_per_block must be >= 1");
   PF_REQUIRE(n_blocks >= 1, PF_ERR_SHAPE, "n_blocks must be >= 1");
   PF_REQUIRE(rope_base > 1.0, PF_ERR_RANGE, "rope_base must be > 1");
+  PF_REQUIRE(n_batch >= 1 && n_batch <= PF_MAX_BATCH, PF_ERR_RANGE, "n_batch must be in [1, %d] (got %d)",
+             PF_MAX_BATCH, n_batch);
   if (block_ids == nullptr)
     PF_REQUIRE(n_shift <= n_blocks, PF_ERR_RANGE, "n_shift (%d) exceeds n_blocks without block_ids", n_shift);
   PF_REQUIRE(n_shift <= 65535, PF_ERR_UNSUPPORTED, "n_shift must be <= 65535");
+  if (n_batch > 1) {
+    PF_REQUIRE(k_batch_stride >= rows_per_block * n_blocks * n_heads * PF_HEAD_DIM, PF_ERR_SHAPE,
+               "k_batch_stride (%lld) is smaller than one cache's keys", static_cast<long long>(k_batch_stride));
+    PF_REQUIRE(k_batch_stride % 8 == 0, PF_ERR_MISALIGNED, "k_batch_stride must be a multiple of 8 elements");
+  }
   if (n_shift == 0) return pf::ok();
   PF_REQUIRE_PTR(k);
   PF_REQUIRE_PTR(deltas);
@@ -112,8 +135,16 @@ extern "C" pf_status pf_rope_shift(pf_bf16* k, int n_heads, int64_t rows_per_blo
   const int64_t rh_per_block = rows_per_block * n_heads;
   const int64_t gx = (rh_per_block + kRowHeadsPerBlock - 1) / kRowHeadsPerBlock;
   PF_REQUIRE(gx <= 0x7FFFFFFF, PF_ERR_UNSUPPORTED, "block too large");
-  dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(n_shift));
+  dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(n_shift), static_cast<unsigned>(n_batch));
   hipLaunchKernelGGL(rope_shift_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     reinterpret_cast<uint16_t*>(k), rh_per_block, n_blocks, block_ids, deltas, rope_base);
+                     reinterpret_cast<uint16_t*>(k), n_batch > 1 ? k_batch_stride : 0, rh_per_block, n_blocks,
+                     block_ids, deltas, n_shift, rope_base);
   return pf::launch_status("pf_rope_shift");
+}
+
+extern "C" pf_status pf_rope_shift(pf_bf16* k, int n_heads, int64_t rows_per_block, int64_t n_blocks,
+                                   const int32_t* block_ids, const int32_t* deltas, int n_shift,
+                                   double rope_base, void* stream) {
+  return pf_rope_shift_batched(k, 0, n_heads, rows_per_block, n_blocks, block_ids, deltas, n_shift, 1, rope_base,
+                               stream);
 }

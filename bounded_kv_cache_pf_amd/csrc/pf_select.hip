@@ -9,15 +9,17 @@
 // end before the recent block and each one's temporal shift is returned.
 //
 // The scoring reads Q and the whole pool once (HBM-bound), in four launches on
-// one stream:
+// one stream; every launch covers a batch of independent caches (grid y):
 //   1. colsum: every workgroup sums a segment of rows (a 64-row slice of Q, or a
 //      slice of one pool block) column by column into fp32 partials;
-//   2. qsum:   the Q partials are added in segment order;
+//   2. qsum:   the Q partials are added per column, 16 interleaved runs of
+//              segments combined in a fixed order;
 //   3. score:  one workgroup per block adds its slices and dots with the Q sum;
-//   4. topk:   one workgroup bitonic-sorts (score desc, index asc) keys in LDS
-//              and writes the first k ids in ascending order.
-// Every sum runs in a fixed order, so identical blocks get identical scores
-// and repeated calls give identical bits.
+//   4. topk:   one workgroup per cache bitonic-sorts (score desc, index asc)
+//              keys in LDS and writes the first k ids in ascending order.
+// Every sum runs in a fixed order that does not depend on the batch, so
+// identical blocks get identical scores, repeated calls give identical bits,
+// and a batched call gives the bits of the single calls.
 #include <math.h>
 
 #include "pf_internal.h"
@@ -26,6 +28,11 @@ namespace {
 
 constexpr int kQSegRows = 64;      // rows of Q per colsum workgroup
 constexpr int kTargetSegments = 512;
+constexpr int kRowUnroll = 4;      // rows whose loads a colsum thread keeps in flight
+constexpr int kQsumCols = 64;      // columns per qsum workgroup
+constexpr int kQsumRuns = 16;      // interleaved runs of Q segments per column
+constexpr int kScoreThreads = 256;
+constexpr int kScoreColsPerThread = PF_MAX_HEADS * PF_HEAD_DIM / kScoreThreads;   // 16
 
 struct SelectPlan {
   int H, cw;          // heads, 16-byte column chunks per row (H*16)
@@ -35,10 +42,12 @@ struct SelectPlan {
   int n_blocks, n_c;
   int ksub;           // slices per pool block
   int sub_rows;       // rows per slice (last slice may be shorter)
-  size_t off_partials, off_qsum, off_scores, bytes;
+  int n_seg;          // segments per cache
+  size_t cache_partials, cache_floats;   // floats per cache: partials, then qsum, then scores
+  size_t bytes;
 };
 
-SelectPlan make_plan(int64_t n_q, int H, int n_blocks, int n_c) {
+SelectPlan make_plan(int64_t n_q, int H, int n_blocks, int n_c, int n_batch) {
   SelectPlan p{};
   p.H = H;
   p.cw = H * 16;
@@ -54,42 +63,60 @@ SelectPlan make_plan(int64_t n_q, int H, int n_blocks, int n_c) {
   if (ksub < 1) ksub = 1;
   p.sub_rows = (n_c + ksub - 1) / ksub;
   p.ksub = (n_c + p.sub_rows - 1) / p.sub_rows;
+  p.n_seg = p.nq_seg + n_blocks * p.ksub;
   const size_t cols = static_cast<size_t>(H) * PF_HEAD_DIM;
-  const size_t n_seg = static_cast<size_t>(p.nq_seg) + static_cast<size_t>(n_blocks) * p.ksub;
-  p.off_partials = 0;
-  p.off_qsum = n_seg * cols * sizeof(float);
-  p.off_scores = p.off_qsum + cols * sizeof(float);
-  p.bytes = p.off_scores + static_cast<size_t>(n_blocks) * sizeof(float);
-  p.bytes = (p.bytes + 255) & ~static_cast<size_t>(255);
+  p.cache_partials = static_cast<size_t>(p.n_seg) * cols;
+  p.cache_floats = p.cache_partials + cols + static_cast<size_t>(n_blocks);
+  p.cache_floats = (p.cache_floats + 63) & ~static_cast<size_t>(63);   // 256-byte aligned per cache
+  p.bytes = p.cache_floats * sizeof(float) * static_cast<size_t>(n_batch);
   return p;
 }
 
 // 1. Column sums of row segments. blockDim = (cw, rpar); thread (x, y) owns the
-// 8 columns of chunk x and rows y, y+rpar, ... of its segment.
-__global__ void colsum_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
-                              float* __restrict__ partials, int64_t n_q, int nq_seg, int n_c,
-                              int ksub, int sub_rows) {
+// 8 columns of chunk x and rows y, y+rpar, ... of its segment, added in row
+// order (loads run kRowUnroll rows ahead). blockIdx.y is the cache.
+__global__ __launch_bounds__(1024) void colsum_kernel(const uint16_t* __restrict__ q, int64_t q_bstride,
+                                                      const uint16_t* __restrict__ pool, int64_t pool_bstride,
+                                                      float* __restrict__ ws, int64_t cache_floats, int64_t n_q,
+                                                      int nq_seg, int n_c, int ksub, int sub_rows) {
   extern __shared__ float red[];   // [rpar][cw*8]
   const int cw = blockDim.x, rpar = blockDim.y;
   const int x = threadIdx.x, y = threadIdx.y;
   const int seg = blockIdx.x;
+  const int64_t b = blockIdx.y;
   const uint16_t* base;
   int64_t rows;
   if (seg < nq_seg) {
     const int64_t r0 = static_cast<int64_t>(seg) * kQSegRows;
     rows = n_q - r0 < kQSegRows ? n_q - r0 : kQSegRows;
-    base = q + r0 * cw * 8;
+    base = q + b * q_bstride + r0 * cw * 8;
   } else {
     const int s = seg - nq_seg;
     const int blk = s / ksub, sub = s % ksub;
     const int r_in = sub * sub_rows;
     rows = n_c - r_in < sub_rows ? n_c - r_in : sub_rows;
-    base = pool + (static_cast<int64_t>(blk) * n_c + r_in) * cw * 8;
+    base = pool + b * pool_bstride + (static_cast<int64_t>(blk) * n_c + r_in) * cw * 8;
   }
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int64_t stride = static_cast<int64_t>(cw) * 8;
-  for (int64_t r = y; r < rows; r += rpar) {
-    const uint4 w = *reinterpret_cast<const uint4*>(base + r * stride + x * 8);
+  const uint16_t* p = base + x * 8;
+  int64_t r = y;
+  for (; r + (kRowUnroll - 1) * rpar < rows; r += kRowUnroll * rpar) {
+    uint4 w[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) w[u] = *reinterpret_cast<const uint4*>(p + (r + u * rpar) * stride);
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += pf::bf16_to_f32(static_cast<uint16_t>(ww[i] & 0xFFFFu));
+        acc[2 * i + 1] += pf::bf16_to_f32(static_cast<uint16_t>(ww[i] >> 16));
+      }
+    }
+  }
+  for (; r < rows; r += rpar) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p + r * stride);
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -104,45 +131,85 @@ __global__ void colsum_kernel(const uint16_t* __restrict__ q, const uint16_t* __
     for (int yy = 1; yy < rpar; ++yy)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += red[(yy * cw + x) * 8 + i];
-    float* out = partials + static_cast<int64_t>(seg) * stride + x * 8;
+    float* out = ws + b * cache_floats + static_cast<int64_t>(seg) * stride + x * 8;
     reinterpret_cast<float4*>(out)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     reinterpret_cast<float4*>(out)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
-// 2. Q sum: column c = sum over Q segments, in segment order.
-__global__ __launch_bounds__(256) void qsum_kernel(const float* __restrict__ partials, float* __restrict__ qsum,
-                                                   int nq_seg, int cols) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= cols) return;
+// 2. Q sum. Thread (c, g) adds segments g, g+16, g+32, ... of column c in
+// order; the 16 runs are then added in order g = 0..15.
+__global__ __launch_bounds__(kQsumCols * kQsumRuns) void qsum_kernel(float* __restrict__ ws, int64_t cache_floats,
+                                                                     int64_t qsum_off, int nq_seg, int cols) {
+  __shared__ float red[kQsumRuns][kQsumCols];
+  const int tc = threadIdx.x % kQsumCols;
+  const int g = threadIdx.x / kQsumCols;
+  const int c = blockIdx.x * kQsumCols + tc;
+  float* cache = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
   float s = 0.f;
-  for (int i = 0; i < nq_seg; ++i) s += partials[static_cast<int64_t>(i) * cols + c];
-  qsum[c] = s;
+  if (c < cols) {
+    int i = g;
+    for (; i + 3 * kQsumRuns < nq_seg; i += 4 * kQsumRuns) {
+      const float a0 = cache[static_cast<int64_t>(i) * cols + c];
+      const float a1 = cache[static_cast<int64_t>(i + kQsumRuns) * cols + c];
+      const float a2 = cache[static_cast<int64_t>(i + 2 * kQsumRuns) * cols + c];
+      const float a3 = cache[static_cast<int64_t>(i + 3 * kQsumRuns) * cols + c];
+      s += a0;
+      s += a1;
+      s += a2;
+      s += a3;
+    }
+    for (; i < nq_seg; i += kQsumRuns) s += cache[static_cast<int64_t>(i) * cols + c];
+  }
+  red[g][tc] = s;
+  __syncthreads();
+  if (g == 0 && c < cols) {
+    float t = red[0][tc];
+#pragma unroll
+    for (int j = 1; j < kQsumRuns; ++j) t += red[j][tc];
+    cache[qsum_off + c] = t;
+  }
 }
 
-// 3. Block score: one workgroup per pool block.
-__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ partials, const float* __restrict__ qsum,
-                                                    float* __restrict__ scores, float* __restrict__ scores_out,
-                                                    int nq_seg, int ksub, int cols, float norm) {
-  __shared__ float red[256];
+// 3. Block score: one workgroup per pool block and cache. Thread t owns the
+// columns t + 256 i; each column's slices are added in slice order, then the
+// products with the Q sum in column order, then a fixed tree over threads.
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(float* __restrict__ ws, int64_t cache_floats,
+                                                              int64_t qsum_off, int64_t scores_off,
+                                                              float* __restrict__ scores_out, int n_blocks,
+                                                              int nq_seg, int ksub, int cols, float norm) {
+  __shared__ float red[kScoreThreads];
   const int blk = blockIdx.x;
-  const float* kp = partials + (static_cast<int64_t>(nq_seg) + static_cast<int64_t>(blk) * ksub) * cols;
-  float dot = 0.f;
-  for (int c = threadIdx.x; c < cols; c += blockDim.x) {
-    float ks = 0.f;
-    for (int s = 0; s < ksub; ++s) ks += kp[static_cast<int64_t>(s) * cols + c];
-    dot += qsum[c] * ks;
+  const int t = threadIdx.x;
+  float* cache = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
+  const float* kp = cache + (static_cast<int64_t>(nq_seg) + static_cast<int64_t>(blk) * ksub) * cols;
+  float ks[kScoreColsPerThread];
+#pragma unroll
+  for (int i = 0; i < kScoreColsPerThread; ++i) ks[i] = 0.f;
+  for (int s = 0; s < ksub; ++s) {
+    const float* row = kp + static_cast<int64_t>(s) * cols;
+#pragma unroll
+    for (int i = 0; i < kScoreColsPerThread; ++i) {
+      const int c = t + kScoreThreads * i;
+      if (c < cols) ks[i] += row[c];
+    }
   }
-  red[threadIdx.x] = dot;
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kScoreColsPerThread; ++i) {
+    const int c = t + kScoreThreads * i;
+    if (c < cols) dot += cache[qsum_off + c] * ks[i];
+  }
+  red[t] = dot;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+  for (int w = kScoreThreads / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     const float s = red[0] * norm;
-    scores[blk] = s;
-    if (scores_out) scores_out[blk] = s;
+    cache[scores_off + blk] = s;
+    if (scores_out) scores_out[static_cast<int64_t>(blockIdx.y) * n_blocks + blk] = s;
   }
 }
 
@@ -154,13 +221,16 @@ __device__ __forceinline__ uint64_t rank_key(float s, uint32_t idx) {
   return (static_cast<uint64_t>(~u) << 32) | idx;
 }
 
-// 4. Top-k: bitonic sort of up to PF_MAX_BLOCKS keys in LDS, one workgroup.
+// 4. Top-k: bitonic sort of up to PF_MAX_BLOCKS keys in LDS, one workgroup per cache.
 constexpr int kTopkThreads = 1024;
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int n_blocks,
-                                                             int top_k, int32_t* __restrict__ ids_out) {
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ ws, int64_t cache_floats,
+                                                             int64_t scores_off, int n_blocks, int top_k,
+                                                             int32_t* __restrict__ ids_out) {
   __shared__ uint64_t keys[PF_MAX_BLOCKS];
   __shared__ uint32_t chosen[PF_MAX_TOPK];
+  const float* scores = ws + static_cast<int64_t>(blockIdx.x) * cache_floats + scores_off;
+  int32_t* ids = ids_out + static_cast<int64_t>(blockIdx.x) * top_k;
   int P = 1;
   while (P < n_blocks) P <<= 1;
   for (int i = threadIdx.x; i < P; i += blockDim.x)
@@ -188,37 +258,51 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     const uint32_t me = chosen[threadIdx.x];
     int rank = 0;
     for (int r = 0; r < top_k; ++r) rank += chosen[r] < me;
-    ids_out[rank] = static_cast<int32_t>(me);
+    ids[rank] = static_cast<int32_t>(me);
   }
 }
 
+// Placement, one workgroup per cache.
 __global__ __launch_bounds__(PF_MAX_TOPK) void deltas_kernel(const int32_t* __restrict__ ids, int top_k,
                                                              int32_t* __restrict__ tags, int n_blocks,
                                                              int32_t recent_first_frame, int32_t block_frames,
                                                              int32_t* __restrict__ deltas) {
   const int r = threadIdx.x;
   if (r >= top_k) return;
-  const int32_t id = ids[r];
+  const int64_t b = blockIdx.x;
+  const int32_t id = ids[b * top_k + r];
   if (id < 0 || id >= n_blocks) {
-    deltas[r] = 0;
+    deltas[b * top_k + r] = 0;
     return;
   }
   const int32_t target = recent_first_frame - (top_k - r) * block_frames;
-  deltas[r] = target - tags[id];
-  tags[id] = target;
+  int32_t* t = tags + b * n_blocks + id;
+  deltas[b * top_k + r] = target - *t;
+  *t = target;
+}
+
+bool valid_sizes(int64_t n_q, int n_heads, int n_blocks, int n_c, int n_batch) {
+  return n_q >= 1 && n_heads >= 1 && n_heads <= PF_MAX_HEADS && n_blocks >= 1 && n_blocks <= PF_MAX_BLOCKS &&
+         n_c >= 1 && n_batch >= 1 && n_batch <= PF_MAX_BATCH;
 }
 
 }  // namespace
 
-extern "C" size_t pf_score_select_workspace_bytes(int64_t n_q, int n_heads, int n_blocks, int n_c) {
-  if (n_q < 1 || n_heads < 1 || n_heads > PF_MAX_HEADS || n_blocks < 1 || n_blocks > PF_MAX_BLOCKS || n_c < 1)
-    return 0;
-  return make_plan(n_q, n_heads, n_blocks, n_c).bytes;
+extern "C" size_t pf_score_select_batched_workspace_bytes(int64_t n_q, int n_heads, int n_blocks, int n_c,
+                                                          int n_batch) {
+  if (!valid_sizes(n_q, n_heads, n_blocks, n_c, n_batch)) return 0;
+  return make_plan(n_q, n_heads, n_blocks, n_c, n_batch).bytes;
 }
 
-extern "C" pf_status pf_score_select(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* pool_k,
-                                     int n_blocks, int n_c, int top_k, int32_t* ids_out, float* scores_out,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" size_t pf_score_select_workspace_bytes(int64_t n_q, int n_heads, int n_blocks, int n_c) {
+  return pf_score_select_batched_workspace_bytes(n_q, n_heads, n_blocks, n_c, 1);
+}
+
+extern "C" pf_status pf_score_select_batched(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, int n_heads,
+                                             const pf_bf16* pool_k, int64_t pool_batch_stride, int n_blocks,
+                                             int n_c, int top_k, int n_batch, int32_t* ids_out,
+                                             float* scores_out, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
   PF_REQUIRE_PTR(q);
   PF_REQUIRE_PTR(pool_k);
   PF_REQUIRE_PTR(ids_out);
@@ -230,13 +314,24 @@ extern "C" pf_status pf_score_select(const pf_bf16* q, int64_t n_q, int n_heads,
              "n_blocks must be in [1, %d] (got %d)", PF_MAX_BLOCKS, n_blocks);
   PF_REQUIRE(top_k >= 1 && top_k <= n_blocks && top_k <= PF_MAX_TOPK, PF_ERR_RANGE,
              "top_k must be in [1, min(n_blocks, %d)] (got %d)", PF_MAX_TOPK, top_k);
+  PF_REQUIRE(n_batch >= 1 && n_batch <= PF_MAX_BATCH, PF_ERR_RANGE, "n_batch must be in [1, %d] (got %d)",
+             PF_MAX_BATCH, n_batch);
   PF_REQUIRE(n_q <= (int64_t{1} << 40), PF_ERR_UNSUPPORTED, "n_q too large");
+  const int64_t row = static_cast<int64_t>(n_heads) * PF_HEAD_DIM;
+  if (n_batch > 1) {
+    PF_REQUIRE(q_batch_stride >= n_q * row, PF_ERR_SHAPE, "q_batch_stride (%lld) is smaller than one cache's Q",
+               static_cast<long long>(q_batch_stride));
+    PF_REQUIRE(pool_batch_stride >= static_cast<int64_t>(n_blocks) * n_c * row, PF_ERR_SHAPE,
+               "pool_batch_stride (%lld) is smaller than one cache's pool", static_cast<long long>(pool_batch_stride));
+    PF_REQUIRE(q_batch_stride % 8 == 0 && pool_batch_stride % 8 == 0, PF_ERR_MISALIGNED,
+               "batch strides must be multiples of 8 elements (16 bytes)");
+  }
   PF_REQUIRE_ALIGNED(q);
   PF_REQUIRE_ALIGNED(pool_k);
   PF_REQUIRE((reinterpret_cast<uintptr_t>(ids_out) & 3u) == 0, PF_ERR_MISALIGNED, "ids_out is not 4-byte aligned");
   PF_REQUIRE((reinterpret_cast<uintptr_t>(scores_out) & 3u) == 0, PF_ERR_MISALIGNED,
              "scores_out is not 4-byte aligned");
-  const SelectPlan p = make_plan(n_q, n_heads, n_blocks, n_c);
+  const SelectPlan p = make_plan(n_q, n_heads, n_blocks, n_c, n_batch);
   PF_REQUIRE(workspace != nullptr, PF_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", p.bytes);
   PF_REQUIRE(workspace_bytes >= p.bytes, PF_ERR_WORKSPACE, "workspace has %zu bytes, need %zu",
              workspace_bytes, p.bytes);
@@ -245,34 +340,44 @@ extern "C" pf_status pf_score_select(const pf_bf16* q, int64_t n_q, int n_heads,
              PF_ERR_UNSUPPORTED, "too many segments");
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  float* partials = reinterpret_cast<float*>(ws + p.off_partials);
-  float* qsum = reinterpret_cast<float*>(ws + p.off_qsum);
-  float* scores = reinterpret_cast<float*>(ws + p.off_scores);
+  float* ws = static_cast<float*>(workspace);
   const int cols = n_heads * PF_HEAD_DIM;
-  const int n_seg = p.nq_seg + n_blocks * p.ksub;
+  const int64_t cf = static_cast<int64_t>(p.cache_floats);
+  const int64_t qsum_off = static_cast<int64_t>(p.cache_partials);
+  const int64_t scores_off = qsum_off + cols;
+  const int64_t qs = n_batch > 1 ? q_batch_stride : 0;
+  const int64_t ps = n_batch > 1 ? pool_batch_stride : 0;
 
   const size_t lds = static_cast<size_t>(p.rpar) * p.cw * 8 * sizeof(float);
-  hipLaunchKernelGGL(colsum_kernel, dim3(n_seg), dim3(p.cw, p.rpar), lds, st,
-                     reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(pool_k), partials,
-                     n_q, p.nq_seg, n_c, p.ksub, p.sub_rows);
+  hipLaunchKernelGGL(colsum_kernel, dim3(p.n_seg, n_batch), dim3(p.cw, p.rpar), lds, st,
+                     reinterpret_cast<const uint16_t*>(q), qs, reinterpret_cast<const uint16_t*>(pool_k), ps, ws,
+                     cf, n_q, p.nq_seg, n_c, p.ksub, p.sub_rows);
   pf_status s = pf::launch_status("pf_score_select (colsum)");
   if (s != PF_OK) return s;
-  hipLaunchKernelGGL(qsum_kernel, dim3((cols + 255) / 256), dim3(256), 0, st, partials, qsum, p.nq_seg, cols);
+  hipLaunchKernelGGL(qsum_kernel, dim3((cols + kQsumCols - 1) / kQsumCols, n_batch), dim3(kQsumCols * kQsumRuns), 0,
+                     st, ws, cf, qsum_off, p.nq_seg, cols);
   s = pf::launch_status("pf_score_select (qsum)");
   if (s != PF_OK) return s;
   const double norm = 1.0 / (static_cast<double>(n_q) * n_c * n_heads * sqrt(static_cast<double>(PF_HEAD_DIM)));
-  hipLaunchKernelGGL(score_kernel, dim3(n_blocks), dim3(256), 0, st, partials, qsum, scores, scores_out,
-                     p.nq_seg, p.ksub, cols, static_cast<float>(norm));
+  hipLaunchKernelGGL(score_kernel, dim3(n_blocks, n_batch), dim3(kScoreThreads), 0, st, ws, cf, qsum_off,
+                     scores_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols, static_cast<float>(norm));
   s = pf::launch_status("pf_score_select (score)");
   if (s != PF_OK) return s;
-  hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(kTopkThreads), 0, st, scores, n_blocks, top_k, ids_out);
+  hipLaunchKernelGGL(topk_kernel, dim3(n_batch), dim3(kTopkThreads), 0, st, ws, cf, scores_off, n_blocks, top_k,
+                     ids_out);
   return pf::launch_status("pf_score_select (topk)");
 }
 
-extern "C" pf_status pf_selection_deltas(const int32_t* ids, int top_k, int32_t* pos_tags, int n_blocks,
-                                         int32_t recent_first_frame, int32_t block_frames, int32_t* deltas_out,
-                                         void* stream) {
+extern "C" pf_status pf_score_select(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* pool_k,
+                                     int n_blocks, int n_c, int top_k, int32_t* ids_out, float* scores_out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return pf_score_select_batched(q, 0, n_q, n_heads, pool_k, 0, n_blocks, n_c, top_k, 1, ids_out, scores_out,
+                                 workspace, workspace_bytes, stream);
+}
+
+extern "C" pf_status pf_selection_deltas_batched(const int32_t* ids, int top_k, int32_t* pos_tags, int n_blocks,
+                                                 int32_t recent_first_frame, int32_t block_frames, int n_batch,
+                                                 int32_t* deltas_out, void* stream) {
   PF_REQUIRE_PTR(ids);
   PF_REQUIRE_PTR(pos_tags);
   PF_REQUIRE_PTR(deltas_out);
@@ -280,10 +385,19 @@ extern "C" pf_status pf_selection_deltas(const int32_t* ids, int top_k, int32_t*
   PF_REQUIRE(top_k >= 1 && top_k <= PF_MAX_TOPK && top_k <= n_blocks, PF_ERR_RANGE,
              "top_k must be in [1, min(n_blocks, %d)] (got %d)", PF_MAX_TOPK, top_k);
   PF_REQUIRE(block_frames >= 1, PF_ERR_RANGE, "block_frames must be >= 1");
+  PF_REQUIRE(n_batch >= 1 && n_batch <= PF_MAX_BATCH, PF_ERR_RANGE, "n_batch must be in [1, %d] (got %d)",
+             PF_MAX_BATCH, n_batch);
   PF_REQUIRE(((reinterpret_cast<uintptr_t>(ids) | reinterpret_cast<uintptr_t>(pos_tags) |
                reinterpret_cast<uintptr_t>(deltas_out)) & 3u) == 0,
              PF_ERR_MISALIGNED, "int32 arrays must be 4-byte aligned");
-  hipLaunchKernelGGL(deltas_kernel, dim3(1), dim3(PF_MAX_TOPK), 0, static_cast<hipStream_t>(stream), ids, top_k,
-                     pos_tags, n_blocks, recent_first_frame, block_frames, deltas_out);
+  hipLaunchKernelGGL(deltas_kernel, dim3(n_batch), dim3(PF_MAX_TOPK), 0, static_cast<hipStream_t>(stream), ids,
+                     top_k, pos_tags, n_blocks, recent_first_frame, block_frames, deltas_out);
   return pf::launch_status("pf_selection_deltas");
+}
+
+extern "C" pf_status pf_selection_deltas(const int32_t* ids, int top_k, int32_t* pos_tags, int n_blocks,
+                                         int32_t recent_first_frame, int32_t block_frames, int32_t* deltas_out,
+                                         void* stream) {
+  return pf_selection_deltas_batched(ids, top_k, pos_tags, n_blocks, recent_first_frame, block_frames, 1,
+                                     deltas_out, stream);
 }

@@ -50,6 +50,7 @@ extern "C" {
 #define PF_MAX_BLOCKS 4096   /* pool blocks scored by pf_score_select */
 #define PF_MAX_TOPK 256      /* top_k of pf_score_select */
 #define PF_MAX_SELECTED 1024 /* n_sel of pf_partition_attn */
+#define PF_MAX_BATCH 65535   /* n_batch of the _batched calls */
 
 typedef uint16_t pf_bf16;
 
@@ -103,6 +104,20 @@ pf_status pf_score_select(const pf_bf16* q, int64_t n_q, int n_heads,
                           int32_t* ids_out, float* scores_out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Batched form: n_batch independent caches (for example the same layer of
+ * several videos, or layers whose queries are already known) in one launch
+ * sequence. Cache b reads q + b*q_batch_stride and pool_k + b*pool_batch_stride
+ * (strides in elements, multiples of 8, each at least one cache's rows; ignored
+ * when n_batch == 1) and writes ids_out[b*top_k ..] and scores_out[b*n_blocks ..].
+ * Every cache gets bit for bit the result of a single call on it.
+ * Limits as above, plus 1 <= n_batch <= PF_MAX_BATCH. */
+size_t pf_score_select_batched_workspace_bytes(int64_t n_q, int n_heads, int n_blocks, int n_c, int n_batch);
+
+pf_status pf_score_select_batched(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, int n_heads,
+                                  const pf_bf16* pool_k, int64_t pool_batch_stride, int n_blocks, int n_c,
+                                  int top_k, int n_batch, int32_t* ids_out, float* scores_out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------- *
  * Placement of the selected blocks -> per-block temporal shift delta
  * [PackForcing arXiv HTML, "The Position Misalignment Problem" and
@@ -126,6 +141,13 @@ pf_status pf_selection_deltas(const int32_t* ids, int top_k, int32_t* pos_tags, 
                               int32_t recent_first_frame, int32_t block_frames,
                               int32_t* deltas_out, void* stream);
 
+/* Batched form: cache b uses ids[b*top_k ..], pos_tags[b*n_blocks ..] and
+ * deltas_out[b*top_k ..]; all caches share top_k, n_blocks and the frames.
+ * Limits as above, plus 1 <= n_batch <= PF_MAX_BATCH. */
+pf_status pf_selection_deltas_batched(const int32_t* ids, int top_k, int32_t* pos_tags, int n_blocks,
+                                      int32_t recent_first_frame, int32_t block_frames, int n_batch,
+                                      int32_t* deltas_out, void* stream);
+
 /* ------------------------------------------------------------------------- *
  * Incremental temporal RoPE shift, in place
  * [PackForcing digest, 前置知识 RoPE (k^(p) = k_raw e^{i theta p}, and
@@ -143,8 +165,9 @@ pf_status pf_selection_deltas(const int32_t* ids, int top_k, int32_t* pos_tags, 
  *   block_ids   int32[n_shift] (device) — blocks to shift; NULL means blocks
  *               0..n_shift-1 (e.g. a contiguous sink slab as one block).
  *   deltas      int32[n_shift] (device) — shift of each listed block, frames.
- * Entries whose block id is outside [0, n_blocks) are skipped. A block listed
- * twice is rotated twice (the order of the two rotations is unspecified).
+ * Entries whose block id is outside [0, n_blocks) are skipped. Each block may
+ * be listed at most once per call: two entries for one block rotate the same
+ * keys concurrently and leave them undefined.
  * Limits: 1 <= n_heads <= PF_MAX_HEADS, rows_per_block >= 1, n_shift >= 0
  *         (0 enqueues nothing), n_shift <= n_blocks when block_ids is NULL,
  *         rope_base > 1.
@@ -152,6 +175,14 @@ pf_status pf_selection_deltas(const int32_t* ids, int top_k, int32_t* pos_tags, 
 pf_status pf_rope_shift(pf_bf16* k, int n_heads, int64_t rows_per_block, int64_t n_blocks,
                         const int32_t* block_ids, const int32_t* deltas, int n_shift,
                         double rope_base, void* stream);
+
+/* Batched form: cache b shifts k + b*k_batch_stride (elements, a multiple of 8,
+ * at least one cache's n_blocks*rows_per_block rows; ignored when n_batch == 1)
+ * using block_ids[b*n_shift ..] (or blocks 0..n_shift-1 when NULL) and
+ * deltas[b*n_shift ..]. Limits as above, plus 1 <= n_batch <= PF_MAX_BATCH. */
+pf_status pf_rope_shift_batched(pf_bf16* k, int64_t k_batch_stride, int n_heads, int64_t rows_per_block,
+                                int64_t n_blocks, const int32_t* block_ids, const int32_t* deltas, int n_shift,
+                                int n_batch, double rope_base, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * Partition attention over the bounded context

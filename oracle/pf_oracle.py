@@ -232,6 +232,19 @@ def placement_deltas(ids: Sequence[int], pos_tags: np.ndarray, recent_first_fram
     return deltas, tags
 
 
+def rollin(pool_k: np.ndarray, pool_v: np.ndarray, pos_tags: np.ndarray, block_k: np.ndarray,
+           block_v: np.ndarray, first_frame: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Append one compressed block to the mid pool.
+
+    [arXiv] "Dual-Resolution Shifting Mechanism": a block that leaves the recent
+    window enters the mid buffer as its compressed backup. Its keys still carry
+    the positions they were encoded at, so its tag is the first frame the block
+    held as the recent block. Returns (pool_k, pool_v, pos_tags), all new arrays.
+    """
+    return (np.concatenate([pool_k, block_k], axis=0), np.concatenate([pool_v, block_v], axis=0),
+            np.append(np.asarray(pos_tags, dtype=np.int64), np.int64(first_frame)))
+
+
 # ---------------------------------------------------------------------------
 # Attention  [digest] 前置知识 KV缓存 (softmax(Q K^T / sqrt(d_h)) V), 方法步骤详情 (5);
 # [arXiv] "Bounded Attention Context" (C = C_sink || C_mid || C_rc)

@@ -90,6 +90,28 @@ def test_rope_validation(pf):
     assert _err(pf, L.pf_rope_shift(A, 12, 0, 40, B, C, 16, 1e4, None))[0] == "PF_ERR_SHAPE"
 
 
+def test_batched_validation(pf):
+    L = pf.lib
+    one = L.pf_score_select_workspace_bytes(6240, 12, 116, 182)
+    ws30 = L.pf_score_select_batched_workspace_bytes(6240, 12, 116, 182, 30)
+    assert ws30 == 30 * one and one % 256 == 0
+    assert L.pf_score_select_batched_workspace_bytes(6240, 12, 116, 182, 0) == 0
+    qs, ps = 6240 * 12 * 128, 116 * 182 * 12 * 128
+    assert _err(pf, L.pf_score_select_batched(A, qs, 6240, 12, B, ps, 116, 182, 16, 0, C, None, A, ws30,
+                                              None))[0] == "PF_ERR_RANGE"
+    name, msg = _err(pf, L.pf_score_select_batched(A, qs - 8, 6240, 12, B, ps, 116, 182, 16, 30, C, None, A,
+                                                   ws30, None))
+    assert name == "PF_ERR_SHAPE" and "q_batch_stride" in msg
+    assert _err(pf, L.pf_score_select_batched(A, qs + 4, 6240, 12, B, ps, 116, 182, 16, 30, C, None, A, ws30,
+                                              None))[0] == "PF_ERR_MISALIGNED"
+    assert _err(pf, L.pf_score_select_batched(A, qs, 6240, 12, B, ps, 116, 182, 16, 30, C, None, A, ws30 - 1,
+                                              None))[0] == "PF_ERR_WORKSPACE"
+    assert _err(pf, L.pf_selection_deltas_batched(A, 16, B, 116, 480, 4, 0, C, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_rope_shift_batched(A, ps, 12, 182, 116, B, C, 16, 70000, 1e4, None))[0] == "PF_ERR_RANGE"
+    name, msg = _err(pf, L.pf_rope_shift_batched(A, ps - 8, 12, 182, 116, B, C, 16, 30, 1e4, None))
+    assert name == "PF_ERR_SHAPE" and "k_batch_stride" in msg
+
+
 def _attn(pf, **kw):
     args = dict(q=A, n_q=6240, H=12, sk=B, sv=C, ns=12480, pk=B, pv=C, nb=40, nc=182, ids=A, nsel=16,
                 rk=B, rv=C, nr=6240, ck=B, cv=C, ncur=6240, scale=0.0, o=A, lse=None, ws=None, wsb=0)

@@ -3,6 +3,8 @@
 Every stage's output is compared with the oracle's, which follows its own state
 from the same seeded inputs.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -77,3 +79,110 @@ def test_layer_step(cfg):
                                 if cfg.query_offset_std else 0))
         c2 = dict(c, q=q2, pool_k=ref["pool_k"])
         check_step(cfg.name + " step 2", cfg, c2, ref["tags"], dl, dl.step(dev(q2)), rows)
+
+
+def test_full_generation_step_c3():
+    """30 layers x 4 denoising steps at the 116-block pool shapes, then the roll-in
+    of one compressed block per layer and one step of the next block on the
+    117-block pool. Selection, placement and the shift run batched over the
+    layers; every layer's ids, deltas, tags and shifted pool are compared with
+    the oracle at every step, and attention on sampled rows for three layers."""
+    cfg = pfgen.C3
+    L, S, M, n_c, k, Bf, H = cfg.layers, cfg.steps, cfg.pool_blocks, cfg.n_c, cfg.top_k, cfg.block_frames, cfg.heads
+    Sb = cfg.sink_blocks
+    attn_layers = (0, L // 2, L - 1)
+    rows = np.unique(np.r_[0, 127, 128, cfg.n - 1, np.random.default_rng(1).integers(0, cfg.n, 4)])
+    say(f"test_full_generation_step_c3: {L} layers x {S} steps, pool {M} -> {M + 1}")
+
+    pool_rows = (M + 1) * n_c
+    pool_k_dev = torch.zeros((L, pool_rows, H, 128), dtype=torch.int16, device="cuda")
+    pool_v_dev = torch.zeros_like(pool_k_dev)
+    ref_pool_k, ref_pool_v, ref_tags, full = [], [], [], {}
+    for l in range(L):
+        c = pfgen.make_cache(cfg, pfgen.layer_seed(cfg, l))
+        pool_k_dev[l, :M * n_c] = dev(c["pool_k"])
+        pool_v_dev[l, :M * n_c] = dev(c["pool_v"])
+        ref_pool_k.append(c["pool_k"])
+        ref_pool_v.append(c["pool_v"])
+        ref_tags.append(O.initial_pos_tags(M, Sb, Bf))
+        if l in attn_layers:
+            full[l] = {"host": c, "dev": {n: dev(c[n]) for n in ("sink_k", "sink_v", "recent_k", "recent_v",
+                                                                   "cur_k", "cur_v")}}
+    say("  caches ready")
+    tags_dev = dev_i32(np.stack(ref_tags))
+    diverged = set()
+
+    def run_step(step, n_blocks, fr):
+        qs = [pfgen.step_queries(cfg, l, step) for l in range(L)]
+        q_dev = dev(np.stack(qs))
+        view_k = pool_k_dev[:, :n_blocks * n_c]
+        ids, _ = pf.pf_score_select_batched(q_dev, view_k, n_c, k)
+        deltas = pf.pf_selection_deltas_batched(ids, tags_dev, fr, Bf)
+        pf.pf_rope_shift_batched(view_k, n_c, deltas, ids)
+        outs = {}
+        for l in attn_layers:
+            d = full[l]["dev"]
+            outs[l] = pf.pf_partition_attn(q_dev[l], d["sink_k"], d["sink_v"], view_k[l],
+                                           pool_v_dev[l, :n_blocks * n_c], n_c, ids[l], d["recent_k"],
+                                           d["recent_v"], d["cur_k"], d["cur_v"])[0]
+        ids_h, deltas_h, tags_h = ids.cpu().numpy(), deltas.cpu().numpy(), tags_dev.cpu().numpy()
+        pools_h = {l: host(pool_k_dev[l, :n_blocks * n_c]) for l in range(L) if l not in diverged}
+        o_h = {l: host(outs[l])[rows] for l in attn_layers}
+
+        def check_layer(l):
+            """Oracle step of layer l against the device results (runs in a worker thread)."""
+            scores = O.block_scores(qs[l], ref_pool_k[l], n_c)
+            ref_ids = O.select_topk(scores, k)
+            gap = O.topk_gap(scores, k)
+            res = {"flagged": gap < 1e-3, "diverged": False, "attn": None}
+            if ids_h[l].tolist() != ref_ids:
+                assert gap < 1e-3 and O.topk_acceptable(ids_h[l].tolist(), scores, k, 1e-3), (step, l)
+                res["diverged"] = True
+                return res
+            d_ref, ref_tags[l] = O.placement_deltas(ref_ids, ref_tags[l], fr, Bf)
+            assert deltas_h[l].tolist() == d_ref.tolist(), (step, l)
+            assert tags_h[l].tolist() == ref_tags[l].tolist(), (step, l)
+            ref_pool_k[l] = O.rope_shift_blocks(ref_pool_k[l], n_c, ref_ids, d_ref.tolist())
+            got = pools_h[l]
+            sel = np.zeros(n_blocks, bool)
+            sel[ref_ids] = True
+            sel = np.repeat(sel, n_c)
+            assert ulp_diff(got[sel], ref_pool_k[l][sel]).max() <= 1, (step, l)
+            assert np.array_equal(got[~sel], ref_pool_k[l][~sel]), (step, l)
+            if l in attn_layers:
+                cache = dict(full[l]["host"], q=qs[l], pool_k=ref_pool_k[l], pool_v=ref_pool_v[l])
+                ks, vs = O.partitions(cache, n_c, ref_ids)
+                o_ref, _ = O.attn_partitioned(qs[l][rows], ks, vs)
+                res["attn"] = attn_errors(o_h[l], o_ref)
+            return res
+
+        live = [l for l in range(L) if l not in diverged]
+        with ThreadPoolExecutor(max_workers=8) as ex:
+            results = dict(zip(live, ex.map(check_layer, live)))
+        worst = 0.0
+        for l, r in results.items():
+            if r["diverged"]:
+                say(f"  step {step} layer {l}: flagged near-tie chose another valid set; layer no longer compared")
+                diverged.add(l)
+            if r["attn"] is not None:
+                mx, mean, rel = r["attn"]
+                worst = max(worst, mx)
+                assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2, (step, l, mx, mean, rel)
+        say(f"  step {step}: {L - len(diverged)} of {L} layers match the oracle (ids, deltas, tags, pool bits), "
+            f"{sum(r['flagged'] for r in results.values())} flagged near-ties, "
+            f"attention max-abs {worst:.2e} on layers {attn_layers}")
+
+    fr = (Sb + M) * Bf
+    for step in range(S):
+        run_step(step, M, fr)
+    # roll-in: the recent block leaves the window and joins the pool compressed
+    for l in range(L):
+        blk = pfgen.rollin_block(cfg, l)
+        pool_k_dev[l, M * n_c:] = dev(blk["k"])
+        pool_v_dev[l, M * n_c:] = dev(blk["v"])
+        ref_pool_k[l], ref_pool_v[l], ref_tags[l] = O.rollin(ref_pool_k[l], ref_pool_v[l], ref_tags[l], blk["k"],
+                                                             blk["v"], fr)
+    tags_dev = torch.cat([tags_dev, torch.full((L, 1), fr, dtype=torch.int32, device="cuda")], dim=1).contiguous()
+    say("  rolled in one block per layer")
+    run_step(S, M + 1, fr + Bf)
+    assert len(diverged) <= 2

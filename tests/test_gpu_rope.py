@@ -76,3 +76,27 @@ def test_rope_shift_other_base():
     rng = np.random.default_rng(6)
     pool = O.f64_to_bf16(rng.standard_normal((6 * 16, 4, 128)))
     _check(pool, 16, [1, 4], [9, 33], base=500000.0)
+
+
+def test_rope_shift_batched_equals_single_calls():
+    say("test_rope_shift_batched_equals_single_calls")
+    B, M, n_c, H, k = 5, 12, 7, 3, 4
+    rng = np.random.default_rng(11)
+    pools = O.f64_to_bf16(rng.standard_normal((B, M * n_c + 3, H, 128)))   # slabs with 3 spare rows
+    ids = np.stack([np.sort(rng.choice(M, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    deltas = rng.integers(-200, 200, (B, k)).astype(np.int32)
+    ids[2, 1] = M + 5                       # out of range: skipped
+    deltas[3, 0] = 0                        # identity
+    slab = dev(pools)
+    view = slab[:, :M * n_c]
+    pf.pf_rope_shift_batched(view, n_c, dev_i32(deltas), dev_i32(ids))
+    got = host(slab)
+    for b in range(B):
+        one = dev(pools[b, :M * n_c])
+        pf.pf_rope_shift(one, n_c, dev_i32(deltas[b]), dev_i32(ids[b]))
+        assert np.array_equal(got[b, :M * n_c], host(one)), b
+        ok = [i for i in ids[b].tolist() if 0 <= i < M]
+        dl = [int(d) for i, d in zip(ids[b].tolist(), deltas[b].tolist()) if 0 <= i < M]
+        ref = O.rope_shift_blocks(pools[b, :M * n_c], n_c, ok, dl)
+        assert ulp_diff(got[b, :M * n_c], ref).max() <= 1
+        assert np.array_equal(got[b, M * n_c:], pools[b, M * n_c:]), "rows past the view must not move"

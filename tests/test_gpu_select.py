@@ -120,3 +120,28 @@ def test_deltas_invalid_ids():
     # r = 1: target 24 - (3 - 1) * 4 = 16, delta 16 - 4; out-of-range ids get 0
     assert d.cpu().numpy().tolist() == [0, 12, 0]
     assert tags.cpu().numpy().tolist() == [8, 12, 16, 20]
+
+
+def test_select_batched_equals_single_calls():
+    say("test_select_batched_equals_single_calls")
+    cfg = pfgen.C2Q
+    B = 3
+    cs = [pfgen.make(cfg, cfg.seed + b) for b in range(B)]
+    rows = cfg.pool_blocks * cfg.n_c
+    q = dev(np.stack([c["q"] for c in cs]))
+    slab = dev(np.stack([np.concatenate([c["pool_k"], c["pool_k"][:cfg.n_c]]) for c in cs]))  # one spare block
+    ids, scores = pf.pf_score_select_batched(q, slab[:, :rows], cfg.n_c, cfg.top_k)
+    ids, scores = ids.cpu().numpy(), scores.cpu().numpy()
+    for b, c in enumerate(cs):
+        i1, s1 = _select(c, cfg.n_c, cfg.top_k)
+        assert ids[b].tolist() == i1
+        assert np.array_equal(scores[b].view(np.uint32), s1.astype(np.float32).view(np.uint32))
+        _compare(c, cfg.n_c, cfg.top_k)
+    tags = torch.stack([dev_i32(O.initial_pos_tags(cfg.pool_blocks, cfg.sink_blocks, cfg.block_frames))] * B)
+    fr = (cfg.sink_blocks + cfg.pool_blocks) * cfg.block_frames
+    d = pf.pf_selection_deltas_batched(dev_i32(ids), tags, fr, cfg.block_frames).cpu().numpy()
+    for b in range(B):
+        d_ref, t_ref = O.placement_deltas(ids[b].tolist(), O.initial_pos_tags(cfg.pool_blocks, cfg.sink_blocks,
+                                                                              cfg.block_frames), fr, cfg.block_frames)
+        assert d[b].tolist() == d_ref.tolist()
+        assert tags[b].cpu().numpy().tolist() == t_ref.tolist()

@@ -106,3 +106,23 @@ def test_placement_repeated_keeps_tags_consistent():
         saw_negative |= bool((d < 0).any())
     assert np.array_equal(tags0 + total, tags)       # a tag is its start plus every shift
     assert saw_negative                               # later steps can move blocks back
+
+
+def test_rollin_block_needs_no_shift_when_selected_last():
+    # the block that just left the recent window sits directly before the new
+    # recent block: chosen in the last slot, its delta is zero; the other
+    # selected blocks are placed exactly as without it
+    M, Sb, Bf, k = 6, 2, 4, 3
+    n_c, H = 2, 1
+    rng = np.random.default_rng(3)
+    pk = rng.integers(0, 1 << 16, (M * n_c, H, 128), dtype=np.uint16)
+    tags = O.initial_pos_tags(M, Sb, Bf)
+    fr = (Sb + M) * Bf
+    blk = rng.integers(0, 1 << 16, (n_c, H, 128), dtype=np.uint16)
+    pk2, pv2, tags2 = O.rollin(pk, pk, tags, blk, blk, fr)
+    assert pk2.shape == ((M + 1) * n_c, H, 128) and np.array_equal(pk2[M * n_c:], blk)
+    assert tags2.tolist() == tags.tolist() + [fr]
+    d, t = O.placement_deltas([1, 4, M], tags2, fr + Bf, Bf)
+    assert d[-1] == 0 and t[M] == fr
+    d_ref, _ = O.placement_deltas([1, 4], tags, fr, Bf)
+    assert d[:2].tolist() == d_ref.tolist()
