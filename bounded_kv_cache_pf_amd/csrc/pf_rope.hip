@@ -9,9 +9,13 @@
 // the correctly rounded rotation of the stored input.
 //
 // HBM-bound: each row-head reads and writes the 88 bytes of its 44 temporal
-// dims. Eight lanes serve one row-head: lanes 0..4 move 16 bytes (dims 8c..8c+7),
-// lane 5 moves 8 bytes (dims 40..43), lanes 6 and 7 idle, so a wave touches
-// eight 256-byte row-heads with full-width vector accesses.
+// dims. Eight lanes serve one row-head: lanes 0..5 move 16 bytes each (dims
+// 8c..8c+7), lanes 6 and 7 idle, so a wave touches eight 256-byte row-heads
+// with full-width vector accesses. Lane 5 rotates dims 40..43 and writes dims
+// 44..47 back with their own bits: every store then covers whole 32-byte
+// sectors (bytes 0..95 of the row-head), which avoids partial-sector writes.
+// Each lane's loads are issued before the workgroup computes its fp64 cos/sin
+// table, so the table's latency hides under the memory latency.
 #include <math.h>
 
 #include "pf_internal.h"
@@ -55,16 +59,8 @@ __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
   const int delta = deltas[entry];
   if (blk < 0 || blk >= n_blocks || delta == 0) return;   // delta 0 is the identity
 
-  __shared__ double cs[kPairs], sn[kPairs];
-  if (threadIdx.x < kPairs) {
-    const double theta = pow(base, -2.0 * threadIdx.x / PF_TEMPORAL_DIMS);
-    sincos(theta * static_cast<double>(delta), &sn[threadIdx.x], &cs[threadIdx.x]);
-  }
-  __syncthreads();
-
   const int sub = threadIdx.x % kLanesPerRowHead;
   const int local = threadIdx.x / kLanesPerRowHead;
-  if (sub > 5) return;
   uint16_t* blk_base = k + blockIdx.z * k_bstride + blk * row_heads_per_block * PF_HEAD_DIM;
   const int64_t rh0 = static_cast<int64_t>(blockIdx.x) * kRowHeadsPerBlock + local;
   // all loads first (kPasses row-heads in flight per lane), then rotate and store
@@ -73,21 +69,22 @@ __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
   for (int pass = 0; pass < kPasses; ++pass) {
     const int64_t rh = rh0 + pass * kRowHeadsPerPass;
     w[pass] = make_uint4(0, 0, 0, 0);
-    if (rh < row_heads_per_block) {
+    if (sub <= 5 && rh < row_heads_per_block) {
       const uint16_t* p = blk_base + rh * PF_HEAD_DIM + sub * 8;
-      if (sub < 5) {
-        w[pass] = *reinterpret_cast<const uint4*>(p);
-      } else {
-        const uint2 h = *reinterpret_cast<const uint2*>(p);
-        w[pass].x = h.x;
-        w[pass].y = h.y;
-      }
+      w[pass] = *reinterpret_cast<const uint4*>(p);
     }
   }
+  __shared__ double cs[kPairs], sn[kPairs];
+  if (threadIdx.x < kPairs) {
+    const double theta = pow(base, -2.0 * threadIdx.x / PF_TEMPORAL_DIMS);
+    sincos(theta * static_cast<double>(delta), &sn[threadIdx.x], &cs[threadIdx.x]);
+  }
+  __syncthreads();
+
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
     const int64_t rh = rh0 + pass * kRowHeadsPerPass;
-    if (rh >= row_heads_per_block) break;
+    if (sub > 5 || rh >= row_heads_per_block) break;
     uint16_t* p = blk_base + rh * PF_HEAD_DIM + sub * 8;
     if (sub < 5) {
       const int j = sub * 4;
@@ -99,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
     } else {
       rotate_pair(w[pass].x, cs[20], sn[20]);
       rotate_pair(w[pass].y, cs[21], sn[21]);
-      *reinterpret_cast<uint2*>(p) = make_uint2(w[pass].x, w[pass].y);
+      *reinterpret_cast<uint4*>(p) = w[pass];
     }
   }
 }

@@ -156,8 +156,10 @@ pf_status pf_selection_deltas_batched(const int32_t* ids, int top_k, int32_t* po
  *
  * For every row of each listed block and every head, the 22 temporal complex
  * pairs (dims 2j, 2j+1 for j < 22) are multiplied by e^{+i theta_j delta} with
- * theta_j = rope_base^(-2j/44); dims 44..127 are not touched, V is never
- * touched, and a zero delta leaves the block's bits unchanged. The angle, its
+ * theta_j = rope_base^(-2j/44); dims 44..127 keep their bits (dims 44..47 are
+ * stored back unchanged together with dims 40..43, so no other writer may
+ * update them concurrently), V is never touched, and a zero delta leaves the
+ * block's bits unchanged. The angle, its
  * cos/sin and the rotation are fp64; the result is rounded once to bf16
  * (round to nearest even).
  *
