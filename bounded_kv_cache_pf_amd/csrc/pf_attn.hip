@@ -27,9 +27,11 @@
 //  * Scheduling: with G resident workgroups and U units, the first
 //    floor(U/G) rounds give every workgroup whole units, numbered so that each
 //    XCD walks consecutive units of one head in lockstep (shared K/V in its
-//    L2). The remaining units are cut into equal runs of key tiles; runs that
-//    cover part of a unit write unnormalised partial results that a small
-//    merge kernel combines. This removes the tail round of idle CUs.
+//    L2). The R remaining units are each cut into the same floor(G/R) key
+//    segments; neighbouring workgroups take the same segment of different
+//    units, so they too read the same keys together. Segments write
+//    unnormalised partial results that a small merge kernel combines. This
+//    removes the tail round of idle CUs.
 #include <math.h>
 
 #include <mutex>
@@ -82,9 +84,8 @@ struct AttnArgs {
   int32_t n_kt;             // key tiles per unit
   int32_t G;                // workgroups in the grid
   int32_t rounds;           // rounds of whole units
-  int32_t n_tail;           // units split into runs (after the whole rounds)
-  int32_t n_chunks;         // runs the split units are cut into (0: none)
-  int64_t tail_tiles;       // n_tail * n_kt
+  int32_t n_tail;           // units cut into key segments (after the whole rounds)
+  int32_t n_seg;            // segments per cut unit (1: the tail units run whole)
   float scale_log2;
 };
 
@@ -401,34 +402,25 @@ __global__ __launch_bounds__(kThreads, kOcc) void partition_attn_kernel(AttnArgs
     if (unit >= a.units) break;
     run_unit(a, sm, unit / a.num_qtiles, static_cast<int64_t>(unit % a.num_qtiles) * kBM, 0, a.n_kt, true, 0);
   }
-  if (slot < a.n_chunks) {
-    const int64_t b = static_cast<int64_t>(slot) * a.tail_tiles / a.n_chunks;
-    const int64_t e = static_cast<int64_t>(slot + 1) * a.tail_tiles / a.n_chunks;
-    for (int64_t it = b; it < e;) {
-      const int64_t tu = it / a.n_kt;                 // split unit index
-      const int64_t u_end = (tu + 1) * a.n_kt;
-      const int64_t seg_end = e < u_end ? e : u_end;
-      const int kt0 = static_cast<int>(it - tu * a.n_kt);
-      const int kt1 = static_cast<int>(seg_end - tu * a.n_kt);
-      const int unit = a.units - a.n_tail + static_cast<int>(tu);
-      const bool whole = kt0 == 0 && kt1 == a.n_kt;
-      run_unit(a, sm, unit / a.num_qtiles, static_cast<int64_t>(unit % a.num_qtiles) * kBM, kt0, kt1, whole,
-               slot + tu);
-      it = seg_end;
-    }
+  // Tail: item i = segment i / n_tail of tail unit i % n_tail. Every tail unit
+  // is cut at the same key tiles and neighbouring slots (one XCD) take the same
+  // segment of different units, so they read the same keys at the same time
+  // and share them in that XCD's L2.
+  if (slot < a.n_seg * a.n_tail) {
+    const int seg = slot / a.n_tail;
+    const int tu = slot - seg * a.n_tail;
+    const int kt0 = static_cast<int>(static_cast<int64_t>(seg) * a.n_kt / a.n_seg);
+    const int kt1 = static_cast<int>(static_cast<int64_t>(seg + 1) * a.n_kt / a.n_seg);
+    const int unit = a.units - a.n_tail + tu;
+    run_unit(a, sm, unit / a.num_qtiles, static_cast<int64_t>(unit % a.num_qtiles) * kBM, kt0, kt1, a.n_seg == 1,
+             slot);
   }
 }
 
-// Merge the partial runs of split units: one workgroup per split unit. Run c
-// covers key tiles [c*T/C, (c+1)*T/C) of the split units' tile sequence, so the
-// run holding tile t is ((t+1)*C - 1) / T.
+// Merge the segments of cut units: one workgroup per cut unit tu, whose
+// segment s wrote partial slot tu + s * n_tail.
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int tu = blockIdx.x;
-  const int64_t first = static_cast<int64_t>(tu) * a.n_kt;
-  const int64_t last = first + a.n_kt - 1;
-  const int c0 = static_cast<int>(((first + 1) * a.n_chunks - 1) / a.tail_tiles);
-  const int c1 = static_cast<int>(((last + 1) * a.n_chunks - 1) / a.tail_tiles);
-  if (c0 == c1) return;   // one run covered the unit and wrote O directly
   const int unit = a.units - a.n_tail + tu;
   const int h = unit / a.num_qtiles;
   const int64_t q0 = static_cast<int64_t>(unit % a.num_qtiles) * kBM;
@@ -437,14 +429,15 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int d0 = (threadIdx.x & 1) * 64;
   const int64_t qrow = q0 + ql;
   float m = -INFINITY;
-  for (int c = c0; c <= c1; ++c) m = fmaxf(m, a.part[(c + tu) * static_cast<int64_t>(kPartFloats) + kBM * D + ql]);
+  for (int c = 0; c < a.n_seg; ++c)
+    m = fmaxf(m, a.part[(tu + static_cast<int64_t>(c) * a.n_tail) * kPartFloats + kBM * D + ql]);
   const float m_use = m == -INFINITY ? 0.f : m;
   float l = 0.f;
   float u[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) u[i] = 0.f;
-  for (int c = c0; c <= c1; ++c) {
-    const float* base = a.part + (c + tu) * static_cast<int64_t>(kPartFloats);
+  for (int c = 0; c < a.n_seg; ++c) {
+    const float* base = a.part + (tu + static_cast<int64_t>(c) * a.n_tail) * kPartFloats;
     const float w = __builtin_amdgcn_exp2f(base[kBM * D + ql] - m_use);
     l += w * base[kBM * D + kBM + ql];
     const float* up = base + static_cast<int64_t>(ql) * D + d0;
@@ -478,8 +471,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 
 struct Plan {
   int64_t units = 0, n_kt = 0;
-  int grid = 0, G = 0, rounds = 0, n_tail = 0, n_chunks = 0;
-  int64_t tail_tiles = 0;
+  int grid = 0, G = 0, rounds = 0, n_tail = 0, n_seg = 0;
   size_t ws_bytes = 0;
 };
 
@@ -501,8 +493,9 @@ int resident_workgroups() {
 }
 
 // rounds of whole units first; a remainder under 3/4 of the machine is cut
-// into runs of key tiles (at least kMinTailTiles each), otherwise it runs as
-// one more round of whole units.
+// into as many equal key segments per unit as the machine holds (each at
+// least kMinTailTiles tiles), otherwise it runs as one more round of whole
+// units.
 Plan make_plan(int64_t n_q, int H, int64_t n_keys, int resident) {
   Plan p;
   p.units = ((n_q + kBM - 1) / kBM) * H;
@@ -512,16 +505,15 @@ Plan make_plan(int64_t n_q, int H, int64_t n_keys, int resident) {
   p.rounds = static_cast<int>(full);
   if (rem > 0 && (rem * 4 < static_cast<int64_t>(resident) * 3 || full == 0)) {
     p.n_tail = static_cast<int>(rem);
-    p.tail_tiles = rem * p.n_kt;
-    int64_t c = p.tail_tiles / kMinTailTiles;
-    if (c > resident) c = resident;
-    if (c < rem) c = rem;
-    p.n_chunks = static_cast<int>(c);
-    p.ws_bytes = static_cast<size_t>(p.n_chunks + p.n_tail) * kPartBytes;
+    int64_t seg = resident / rem;
+    if (seg > p.n_kt / kMinTailTiles) seg = p.n_kt / kMinTailTiles;
+    if (seg < 1) seg = 1;
+    p.n_seg = static_cast<int>(seg);
+    p.ws_bytes = seg > 1 ? static_cast<size_t>(seg * rem) * kPartBytes : 0;
   } else if (rem > 0) {
     p.rounds += 1;
   }
-  p.grid = full > 0 ? resident : p.n_chunks;
+  p.grid = full > 0 ? resident : p.n_seg * p.n_tail;
   p.G = p.grid;
   return p;
 }
@@ -638,15 +630,14 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
   a.G = p.G;
   a.rounds = p.rounds;
   a.n_tail = p.n_tail;
-  a.n_chunks = p.n_chunks;
-  a.tail_tiles = p.tail_tiles;
+  a.n_seg = p.n_seg;
   const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(D));
   a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(partition_attn_kernel, dim3(p.grid), dim3(kThreads), 0, st, a);
   pf_status s = pf::launch_status("pf_partition_attn");
-  if (s != PF_OK || p.n_chunks == 0) return s;
+  if (s != PF_OK || p.n_seg <= 1) return s;
   hipLaunchKernelGGL(merge_kernel, dim3(p.n_tail), dim3(256), 0, st, a);
   return pf::launch_status("pf_partition_attn (merge)");
 }
