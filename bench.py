@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the batched selection/RoPE measurement (profiling the layer-step alone)")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="only run the batched selection/RoPE measurement (for its own profile)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter calibration)")
@@ -179,6 +183,10 @@ def main():
     import bounded_kv_cache_pf_amd as pf
     import pfgen
 
+    if args.batched_only:
+        print(json.dumps({"hbm_batched": hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, args.steps)}), flush=True)
+        return
+
     cfg = pfgen.C1
     t_gen = time.perf_counter()
     cache = pfgen.make(cfg)
@@ -270,7 +278,8 @@ def main():
         "rope_shift_gbs": round(rope_bytes / (ms_rope * 1e-3) / 1e9, 1),
         "input_gen_s": round(t_gen, 2),
     }
-    out["hbm_batched"] = hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, 5)
+    if not args.no_batched:
+        out["hbm_batched"] = hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, 5)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cache, cfg, args.cpu_seconds)
     print(json.dumps(out), flush=True)
