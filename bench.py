@@ -154,6 +154,23 @@ def hbm_batched(pf, torch, cfg_pool, layers, reps):
                           "GB/s": round(rope_bytes / (t[2] * 1e-3) / 1e9, 1),
                           "frac_hbm": round(rope_bytes / (t[2] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
     del q, pk, ws
+    # the pages' eviction event: every layer's sink slab shifted forward by
+    # delta = evicted blocks x B_f, one batched call over the layers
+    sink = (torch.randn((layers, cfg_pool.n_sink, H, 128), generator=g, device="cuda") * s).to(torch.bfloat16)
+    sd = torch.full((layers, 1), 2 * Bf, dtype=torch.int32, device="cuda")
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps + 2)]
+    for i in range(reps + 2):
+        sev[i][0].record(stream)
+        pf.pf_rope_shift_batched(sink, cfg_pool.n_sink, sd)
+        sev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ts = float(np.mean([e[0].elapsed_time(e[1]) for e in sev[2:]]))
+    sink_bytes = layers * cfg_pool.n_sink * H * 2 * 88
+    out["sink_shift"] = {"workload": f"{layers} sink slabs of {cfg_pool.n_sink} rows, one batched call",
+                         "ms": round(ts, 4), "algorithmic_bytes": sink_bytes,
+                         "GB/s": round(sink_bytes / (ts * 1e-3) / 1e9, 1),
+                         "frac_hbm": round(sink_bytes / (ts * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del sink
     return out
 
 
@@ -279,7 +296,12 @@ def main():
         "input_gen_s": round(t_gen, 2),
     }
     if not args.no_batched:
-        out["hbm_batched"] = hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, 5)
+        hb = hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, 5)
+        # one generation step = layers x denoising steps layer-steps; the eviction
+        # shift runs once per step at most
+        gen_ms = pfgen.C3.layers * pfgen.C3.steps * ms_step
+        hb["sink_shift"]["frac_of_generation_step"] = round(hb["sink_shift"]["ms"] / gen_ms, 5)
+        out["hbm_batched"] = hb
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cache, cfg, args.cpu_seconds)
     print(json.dumps(out), flush=True)

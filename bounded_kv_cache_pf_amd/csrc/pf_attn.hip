@@ -417,32 +417,34 @@ __global__ __launch_bounds__(kThreads, kOcc) void partition_attn_kernel(AttnArgs
   }
 }
 
-// Merge the segments of cut units: one workgroup per cut unit tu, whose
-// segment s wrote partial slot tu + s * n_tail.
+// Merge the segments of cut units. Workgroup (tu, y) takes queries
+// 32y .. 32y+31 of cut unit tu, whose segment s wrote partial slot
+// tu + s * n_tail; eight threads share a query, 16 dims each.
+constexpr int kMergeQueries = 32;
+
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int tu = blockIdx.x;
   const int unit = a.units - a.n_tail + tu;
   const int h = unit / a.num_qtiles;
   const int64_t q0 = static_cast<int64_t>(unit % a.num_qtiles) * kBM;
-  // thread t: query t/2, dims (t&1)*64 .. +63
-  const int ql = threadIdx.x >> 1;
-  const int d0 = (threadIdx.x & 1) * 64;
+  const int ql = blockIdx.y * kMergeQueries + (threadIdx.x >> 3);
+  const int d0 = (threadIdx.x & 7) * 16;
   const int64_t qrow = q0 + ql;
   float m = -INFINITY;
   for (int c = 0; c < a.n_seg; ++c)
     m = fmaxf(m, a.part[(tu + static_cast<int64_t>(c) * a.n_tail) * kPartFloats + kBM * D + ql]);
   const float m_use = m == -INFINITY ? 0.f : m;
   float l = 0.f;
-  float u[64];
+  float u[16];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) u[i] = 0.f;
+  for (int i = 0; i < 16; ++i) u[i] = 0.f;
   for (int c = 0; c < a.n_seg; ++c) {
     const float* base = a.part + (tu + static_cast<int64_t>(c) * a.n_tail) * kPartFloats;
     const float w = __builtin_amdgcn_exp2f(base[kBM * D + ql] - m_use);
     l += w * base[kBM * D + kBM + ql];
     const float* up = base + static_cast<int64_t>(ql) * D + d0;
 #pragma unroll
-    for (int i = 0; i < 64; i += 4) {
+    for (int i = 0; i < 16; i += 4) {
       const float4 v = *reinterpret_cast<const float4*>(up + i);
       u[i] += w * v.x;
       u[i + 1] += w * v.y;
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const float inv = l > 0.f ? 1.f / l : 0.f;
   uint16_t* op = a.o + qrow * a.row_stride + static_cast<int64_t>(h) * D + d0;
 #pragma unroll
-  for (int i = 0; i < 64; i += 8) {
+  for (int i = 0; i < 16; i += 8) {
     uint4 w;
     w.x = pf::pack_bf16x2(u[i] * inv, u[i + 1] * inv);
     w.y = pf::pack_bf16x2(u[i + 2] * inv, u[i + 3] * inv);
@@ -638,6 +640,6 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
   hipLaunchKernelGGL(partition_attn_kernel, dim3(p.grid), dim3(kThreads), 0, st, a);
   pf_status s = pf::launch_status("pf_partition_attn");
   if (s != PF_OK || p.n_seg <= 1) return s;
-  hipLaunchKernelGGL(merge_kernel, dim3(p.n_tail), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(merge_kernel, dim3(p.n_tail, kBM / kMergeQueries), dim3(256), 0, st, a);
   return pf::launch_status("pf_partition_attn (merge)");
 }

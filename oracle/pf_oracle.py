@@ -245,6 +245,27 @@ def rollin(pool_k: np.ndarray, pool_v: np.ndarray, pos_tags: np.ndarray, block_k
             np.append(np.asarray(pos_tags, dtype=np.int64), np.int64(first_frame)))
 
 
+def evict_and_shift_sink(sink_k: np.ndarray, pool_k: np.ndarray, pool_v: np.ndarray, pos_tags: np.ndarray,
+                         n_evict: int, n_c: int, block_frames: int,
+                         base: float = ROPE_BASE) -> Dict[str, np.ndarray]:
+    """Evict the n_evict oldest pool blocks and move the sink after them.
+
+    [arXiv] "The Position Misalignment Problem": keeping the mid pool within its
+    budget evicts its oldest compressed blocks, which opens a gap of
+    delta = n_evict * B_f frames between the sink and the first surviving mid
+    block. "Incremental RoPE adjustment": the sink keys are rotated forward by
+    delta on the temporal axis only, so they again sit directly before the mid
+    keys. Pool blocks are in arrival order (block 0 is the oldest). Returns the
+    shifted sink (bf16 bits), the surviving pool K/V and tags, and delta.
+    """
+    delta = int(n_evict) * int(block_frames)
+    rows = sink_k.shape[0]
+    shifted = rope_shift_blocks(sink_k, rows, [0], [delta], base)
+    cut = int(n_evict) * int(n_c)
+    return {"sink_k": shifted, "pool_k": pool_k[cut:], "pool_v": pool_v[cut:],
+            "tags": np.asarray(pos_tags, dtype=np.int64)[int(n_evict):], "delta": delta}
+
+
 # ---------------------------------------------------------------------------
 # Attention  [digest] 前置知识 KV缓存 (softmax(Q K^T / sqrt(d_h)) V), 方法步骤详情 (5);
 # [arXiv] "Bounded Attention Context" (C = C_sink || C_mid || C_rc)

@@ -100,3 +100,25 @@ def test_rope_shift_batched_equals_single_calls():
         ref = O.rope_shift_blocks(pools[b, :M * n_c], n_c, ok, dl)
         assert ulp_diff(got[b, :M * n_c], ref).max() <= 1
         assert np.array_equal(got[b, M * n_c:], pools[b, M * n_c:]), "rows past the view must not move"
+
+
+def test_sink_shift_after_eviction_batched_over_layers():
+    """The pages' eviction event: every layer's sink slab moves forward by
+    delta = evicted blocks x B_f frames, in one batched call (block_ids NULL:
+    the whole slab is one block)."""
+    say("test_sink_shift_after_eviction_batched_over_layers")
+    cfg = pfgen.C1
+    L, n_evict = 3, 2
+    rng = np.random.default_rng(12)
+    sinks = O.f64_to_bf16(rng.standard_normal((L, cfg.n_sink, cfg.heads, 128)) / np.sqrt(2))
+    pool = np.zeros((4 * cfg.n_c, cfg.heads, 128), dtype=np.uint16)
+    tags = O.initial_pos_tags(4, cfg.sink_blocks, cfg.block_frames)
+    ref = [O.evict_and_shift_sink(sinks[l], pool, pool, tags, n_evict, cfg.n_c, cfg.block_frames) for l in range(L)]
+    k = dev(sinks)
+    deltas = dev_i32([[ref[0]["delta"]]] * L)
+    pf.pf_rope_shift_batched(k, cfg.n_sink, deltas)
+    got = host(k)
+    for l in range(L):
+        ud = ulp_diff(got[l], ref[l]["sink_k"])
+        say(f"  layer {l}: delta {ref[l]['delta']}, max ulp {ud.max()}, exact {(ud == 0).mean():.6f}")
+        assert ud.max() <= 1 and (ud == 0).mean() > 0.999

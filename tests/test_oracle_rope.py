@@ -119,3 +119,25 @@ def _mut_pairing(k, d):
 @pytest.mark.parametrize("mutant", [_mut_sign, _mut_all_dims, _mut_freq, _mut_pairing])
 def test_planted_mistakes_fail_identity(mutant):
     assert _max_identity_error(mutant, O.rope_encode, trials=20) > 1e-3
+
+
+def test_evict_and_shift_sink_closes_the_gap():
+    # sink keys encoded at frames 0..S_b*B_f-1 (one row per frame here); after
+    # evicting D blocks they must equal keys encoded at frame + D*B_f, and the
+    # sink's last frame + 1 must be the first surviving block's first frame
+    Sb, Bf, M, n_c, D = 2, 4, 6, 3, 2
+    rng = np.random.default_rng(8)
+    raw = rng.standard_normal((Sb * Bf, 1, O.HEAD_DIM))
+    enc = np.stack([O.rope_encode(raw[f], f, 3, 5) for f in range(Sb * Bf)])
+    sink = O.f64_to_bf16(enc)
+    pool = O.f64_to_bf16(rng.standard_normal((M * n_c, 1, O.HEAD_DIM)))
+    tags = O.initial_pos_tags(M, Sb, Bf)
+    r = O.evict_and_shift_sink(sink, pool, pool, tags, D, n_c, Bf)
+    assert r["delta"] == D * Bf
+    assert r["pool_k"].shape[0] == (M - D) * n_c and r["tags"].tolist() == tags[D:].tolist()
+    assert (Sb * Bf - 1) + r["delta"] + 1 == r["tags"][0]
+    want = np.stack([O.rope_encode(raw[f], f + r["delta"], 3, 5) for f in range(Sb * Bf)])
+    got = O.bf16_to_f64(r["sink_k"])
+    # one bf16 rounding of the stored input plus one of the result
+    assert np.max(np.abs(got - want)) <= 2 * 2.0 ** -8 * np.max(np.abs(want)) + 1e-12
+    assert np.array_equal(r["sink_k"][..., O.T_DIMS:], sink[..., O.T_DIMS:])
