@@ -174,6 +174,42 @@ def hbm_batched(pf, torch, cfg_pool, layers, reps):
     return out
 
 
+def selection_cadence(pf, torch, pfgen, dev, ms_attn, caches=8):
+    """The pages' faster selection (a quarter of the query rows, every other
+    head) against full scoring: time per call on the default layer and how many
+    of the 16 selected blocks agree on caches with clear block preferences
+    (per-head query mean, block-wise key offsets). A FIFO selector (the 16
+    newest blocks) is reported alongside."""
+    cfg = pfgen.C2Q
+    k = cfg.top_k
+    agree_sub, agree_fifo = [], []
+    t_full, t_sub = [], []
+    for i in range(caches):
+        c = pfgen.make(cfg, cfg.seed + 100 + i)
+        q, pk = dev(c["q"]), dev(c["pool_k"])
+        full, _ = pf.pf_score_select(q, pk, cfg.n_c, k)
+        sub, _ = pf.pf_score_select_sub(q, pk, cfg.n_c, k, 4, 2)
+        fs, ss = set(full.cpu().numpy().tolist()), set(sub.cpu().numpy().tolist())
+        agree_sub.append(len(fs & ss) / k)
+        agree_fifo.append(len(fs & set(range(cfg.pool_blocks - k, cfg.pool_blocks))) / k)
+        for fn, acc in ((lambda: pf.pf_score_select(q, pk, cfg.n_c, k), t_full),
+                        (lambda: pf.pf_score_select_sub(q, pk, cfg.n_c, k, 4, 2), t_sub)):
+            fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            acc.append(e0.elapsed_time(e1) / 10)
+    return {"workload": f"{caches} caches at the 116-block pool shapes with a per-head query mean; "
+                        f"sub-sampled = every 4th query row and every other head",
+            "full_ms": round(float(np.median(t_full)), 4), "subsampled_ms": round(float(np.median(t_sub)), 4),
+            "subsampled_topk_agreement": round(float(np.mean(agree_sub)), 4),
+            "fifo_topk_agreement": round(float(np.mean(agree_fifo)), 4),
+            "full_over_attention": round(float(np.median(t_full)) / ms_attn, 4)}
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -295,6 +331,7 @@ def main():
         "rope_shift_gbs": round(rope_bytes / (ms_rope * 1e-3) / 1e9, 1),
         "input_gen_s": round(t_gen, 2),
     }
+    out["selection_cadence"] = selection_cadence(pf, torch, pfgen, dev, ms_attn)
     if not args.no_batched:
         hb = hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, 5)
         # one generation step = layers x denoising steps layer-steps; the eviction

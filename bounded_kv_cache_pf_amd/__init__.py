@@ -37,6 +37,8 @@ _SIGNATURES = {
     "pf_selection_deltas": ([_p, _i32, _p, _i32, ctypes.c_int32, ctypes.c_int32, _p, _p], _i32),
     "pf_rope_shift": ([_p, _i32, _i64, _i64, _p, _p, _i32, ctypes.c_double, _p], _i32),
     "pf_score_select_batched_workspace_bytes": ([_i64, _i32, _i32, _i32, _i32], _sz),
+    "pf_score_select_sub_workspace_bytes": ([_i64, _i32, _i32, _i32, _i32, _i32], _sz),
+    "pf_score_select_sub": ([_p, _i64, _i32, _i32, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _sz, _p], _i32),
     "pf_score_select_batched": ([_p, _i64, _i64, _i32, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _sz, _p],
                                 _i32),
     "pf_selection_deltas_batched": ([_p, _i32, _p, _i32, ctypes.c_int32, ctypes.c_int32, _i32, _p, _p], _i32),
@@ -133,6 +135,30 @@ def pf_score_select(q, pool_k, n_c: int, top_k: int, ids_out=None, scores_out=No
     _check(lib.pf_score_select(_ptr(q), n_q, heads, _ptr(pool_k), n_blocks, n_c, top_k, _ptr(ids_out),
                                _ptr(scores_out), _ptr(workspace), workspace.numel(), _stream(stream)),
            "pf_score_select")
+    return ids_out, scores_out
+
+
+def pf_score_select_sub(q, pool_k, n_c: int, top_k: int, q_step: int, head_step: int, ids_out=None,
+                        scores_out=None, workspace=None, stream=None) -> Tuple[object, object]:
+    """Top-k scored from query rows 0, q_step, ... and heads 0, head_step, ... only."""
+    torch = _torch()
+    heads = int(q.shape[1])
+    n_q = _kv_rows(q, heads, "q")
+    rows = _kv_rows(pool_k, heads, "pool_k")
+    if n_c <= 0 or rows % n_c:
+        raise ValueError("pool rows must be a multiple of n_c")
+    n_blocks = rows // n_c
+    if ids_out is None:
+        ids_out = torch.empty(top_k, dtype=torch.int32, device=q.device)
+    if scores_out is None:
+        scores_out = torch.empty(n_blocks, dtype=torch.float32, device=q.device)
+    _i32_vec(ids_out, "ids_out")
+    need = int(lib.pf_score_select_sub_workspace_bytes(n_q, heads, q_step, head_step, n_blocks, n_c))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.pf_score_select_sub(_ptr(q), n_q, heads, q_step, head_step, _ptr(pool_k), n_blocks, n_c, top_k,
+                                   _ptr(ids_out), _ptr(scores_out), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)), "pf_score_select_sub")
     return ids_out, scores_out
 
 

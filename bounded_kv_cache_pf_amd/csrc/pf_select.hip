@@ -48,8 +48,12 @@ struct SelectPlan {
   size_t bytes;
 };
 
-SelectPlan make_plan(int64_t n_q, int H, int n_blocks, int n_c, int n_batch) {
+// q_step / head_step: score with query rows 0, q_step, 2 q_step, ... and heads
+// 0, head_step, 2 head_step, ... only (1, 1: every query and head).
+SelectPlan make_plan(int64_t n_q, int H, int n_blocks, int n_c, int n_batch, int q_step = 1, int head_step = 1) {
   SelectPlan p{};
+  H = (H + head_step - 1) / head_step;           // heads that are scored
+  n_q = (n_q + q_step - 1) / q_step;             // query rows that are scored
   p.H = H;
   p.cw = H * 16;
   p.rpar = 1024 / p.cw;
@@ -81,28 +85,31 @@ SelectPlan make_plan(int64_t n_q, int H, int n_blocks, int n_c, int n_batch) {
 __global__ __launch_bounds__(1024) void colsum_kernel(const uint16_t* __restrict__ q, int64_t q_bstride,
                                                       const uint16_t* __restrict__ pool, int64_t pool_bstride,
                                                       float* __restrict__ ws, int64_t cache_floats, int64_t n_q,
-                                                      int nq_seg, int n_c, int ksub, int sub_rows) {
+                                                      int nq_seg, int n_c, int ksub, int sub_rows,
+                                                      int64_t row_elems, int q_step, int head_step) {
   extern __shared__ float red[];   // [rpar][cw*8]
   const int cw = blockDim.x, rpar = blockDim.y;
   const int x = threadIdx.x, y = threadIdx.y;
   const int seg = blockIdx.x;
   const int64_t b = blockIdx.y;
   const uint16_t* base;
-  int64_t rows;
+  int64_t rows, stride;   // rows of this segment, elements between them
   if (seg < nq_seg) {
-    const int64_t r0 = static_cast<int64_t>(seg) * kQSegRows;
+    const int64_t r0 = static_cast<int64_t>(seg) * kQSegRows;   // in scored (sub-sampled) rows
     rows = n_q - r0 < kQSegRows ? n_q - r0 : kQSegRows;
-    base = q + b * q_bstride + r0 * cw * 8;
+    stride = row_elems * q_step;
+    base = q + b * q_bstride + r0 * stride;
   } else {
     const int s = seg - nq_seg;
     const int blk = s / ksub, sub = s % ksub;
     const int r_in = sub * sub_rows;
     rows = n_c - r_in < sub_rows ? n_c - r_in : sub_rows;
-    base = pool + b * pool_bstride + (static_cast<int64_t>(blk) * n_c + r_in) * cw * 8;
+    stride = row_elems;
+    base = pool + b * pool_bstride + (static_cast<int64_t>(blk) * n_c + r_in) * row_elems;
   }
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int64_t stride = static_cast<int64_t>(cw) * 8;
-  const uint16_t* p = base + x * 8;
+  // column chunk x: 8 dims of scored head x/16 (head (x/16) * head_step of the row)
+  const uint16_t* p = base + (x >> 4) * head_step * PF_HEAD_DIM + (x & 15) * 8;
   int64_t r = y;
   for (; r + (kRowUnroll - 1) * rpar < rows; r += kRowUnroll * rpar) {
     uint4 w[kRowUnroll];
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(1024) void colsum_kernel(const uint16_t* __restrict
     for (int yy = 1; yy < rpar; ++yy)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += red[(yy * cw + x) * 8 + i];
-    float* out = ws + b * cache_floats + static_cast<int64_t>(seg) * stride + x * 8;
+    float* out = ws + b * cache_floats + static_cast<int64_t>(seg) * cw * 8 + x * 8;
     reinterpret_cast<float4*>(out)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     reinterpret_cast<float4*>(out)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
@@ -304,11 +311,12 @@ extern "C" size_t pf_score_select_workspace_bytes(int64_t n_q, int n_heads, int 
   return pf_score_select_batched_workspace_bytes(n_q, n_heads, n_blocks, n_c, 1);
 }
 
-extern "C" pf_status pf_score_select_batched(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, int n_heads,
-                                             const pf_bf16* pool_k, int64_t pool_batch_stride, int n_blocks,
-                                             int n_c, int top_k, int n_batch, int32_t* ids_out,
-                                             float* scores_out, void* workspace, size_t workspace_bytes,
-                                             void* stream) {
+namespace {
+
+pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, int n_heads, int q_step,
+                       int head_step, const pf_bf16* pool_k, int64_t pool_batch_stride, int n_blocks, int n_c,
+                       int top_k, int n_batch, int32_t* ids_out, float* scores_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   PF_REQUIRE_PTR(q);
   PF_REQUIRE_PTR(pool_k);
   PF_REQUIRE_PTR(ids_out);
@@ -337,7 +345,9 @@ extern "C" pf_status pf_score_select_batched(const pf_bf16* q, int64_t q_batch_s
   PF_REQUIRE((reinterpret_cast<uintptr_t>(ids_out) & 3u) == 0, PF_ERR_MISALIGNED, "ids_out is not 4-byte aligned");
   PF_REQUIRE((reinterpret_cast<uintptr_t>(scores_out) & 3u) == 0, PF_ERR_MISALIGNED,
              "scores_out is not 4-byte aligned");
-  const SelectPlan p = make_plan(n_q, n_heads, n_blocks, n_c, n_batch);
+  PF_REQUIRE(q_step >= 1 && head_step >= 1 && head_step <= n_heads, PF_ERR_RANGE,
+             "q_step must be >= 1 and head_step in [1, n_heads] (got %d, %d)", q_step, head_step);
+  const SelectPlan p = make_plan(n_q, n_heads, n_blocks, n_c, n_batch, q_step, head_step);
   PF_REQUIRE(workspace != nullptr, PF_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", p.bytes);
   PF_REQUIRE(workspace_bytes >= p.bytes, PF_ERR_WORKSPACE, "workspace has %zu bytes, need %zu",
              workspace_bytes, p.bytes);
@@ -347,7 +357,7 @@ extern "C" pf_status pf_score_select_batched(const pf_bf16* q, int64_t q_batch_s
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* ws = static_cast<float*>(workspace);
-  const int cols = n_heads * PF_HEAD_DIM;
+  const int cols = p.H * PF_HEAD_DIM;   // scored heads only
   const int64_t cf = static_cast<int64_t>(p.cache_floats);
   const int64_t qsum_off = static_cast<int64_t>(p.cache_partials);
   const int64_t scores_off = qsum_off + cols;
@@ -357,14 +367,15 @@ extern "C" pf_status pf_score_select_batched(const pf_bf16* q, int64_t q_batch_s
   const size_t lds = static_cast<size_t>(p.rpar) * p.cw * 8 * sizeof(float);
   hipLaunchKernelGGL(colsum_kernel, dim3(p.n_seg, n_batch), dim3(p.cw, p.rpar), lds, st,
                      reinterpret_cast<const uint16_t*>(q), qs, reinterpret_cast<const uint16_t*>(pool_k), ps, ws,
-                     cf, n_q, p.nq_seg, n_c, p.ksub, p.sub_rows);
+                     cf, p.n_q, p.nq_seg, n_c, p.ksub, p.sub_rows, static_cast<int64_t>(n_heads) * PF_HEAD_DIM,
+                     q_step, head_step);
   pf_status s = pf::launch_status("pf_score_select (colsum)");
   if (s != PF_OK) return s;
   hipLaunchKernelGGL(qsum_kernel, dim3((cols + kQsumCols - 1) / kQsumCols, n_batch), dim3(kQsumCols * kQsumRuns), 0,
                      st, ws, cf, qsum_off, p.nq_seg, cols);
   s = pf::launch_status("pf_score_select (qsum)");
   if (s != PF_OK) return s;
-  const double norm = 1.0 / (static_cast<double>(n_q) * n_c * n_heads * sqrt(static_cast<double>(PF_HEAD_DIM)));
+  const double norm = 1.0 / (static_cast<double>(p.n_q) * n_c * p.H * sqrt(static_cast<double>(PF_HEAD_DIM)));
   hipLaunchKernelGGL(score_kernel, dim3(n_blocks, n_batch), dim3(kScoreThreads), 0, st, ws, cf, qsum_off,
                      scores_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols, static_cast<float>(norm));
   s = pf::launch_status("pf_score_select (score)");
@@ -374,11 +385,35 @@ extern "C" pf_status pf_score_select_batched(const pf_bf16* q, int64_t q_batch_s
   return pf::launch_status("pf_score_select (topk)");
 }
 
+}  // namespace
+
+extern "C" pf_status pf_score_select_batched(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, int n_heads,
+                                             const pf_bf16* pool_k, int64_t pool_batch_stride, int n_blocks,
+                                             int n_c, int top_k, int n_batch, int32_t* ids_out,
+                                             float* scores_out, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  return score_select(q, q_batch_stride, n_q, n_heads, 1, 1, pool_k, pool_batch_stride, n_blocks, n_c, top_k,
+                      n_batch, ids_out, scores_out, workspace, workspace_bytes, stream);
+}
+
 extern "C" pf_status pf_score_select(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* pool_k,
                                      int n_blocks, int n_c, int top_k, int32_t* ids_out, float* scores_out,
                                      void* workspace, size_t workspace_bytes, void* stream) {
-  return pf_score_select_batched(q, 0, n_q, n_heads, pool_k, 0, n_blocks, n_c, top_k, 1, ids_out, scores_out,
-                                 workspace, workspace_bytes, stream);
+  return score_select(q, 0, n_q, n_heads, 1, 1, pool_k, 0, n_blocks, n_c, top_k, 1, ids_out, scores_out,
+                      workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t pf_score_select_sub_workspace_bytes(int64_t n_q, int n_heads, int q_step, int head_step,
+                                                      int n_blocks, int n_c) {
+  if (!valid_sizes(n_q, n_heads, n_blocks, n_c, 1) || q_step < 1 || head_step < 1 || head_step > n_heads) return 0;
+  return make_plan(n_q, n_heads, n_blocks, n_c, 1, q_step, head_step).bytes;
+}
+
+extern "C" pf_status pf_score_select_sub(const pf_bf16* q, int64_t n_q, int n_heads, int q_step, int head_step,
+                                         const pf_bf16* pool_k, int n_blocks, int n_c, int top_k, int32_t* ids_out,
+                                         float* scores_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return score_select(q, 0, n_q, n_heads, q_step, head_step, pool_k, 0, n_blocks, n_c, top_k, 1, ids_out,
+                      scores_out, workspace, workspace_bytes, stream);
 }
 
 extern "C" pf_status pf_selection_deltas_batched(const int32_t* ids, int top_k, int32_t* pos_tags, int n_blocks,

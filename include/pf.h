@@ -104,6 +104,20 @@ pf_status pf_score_select(const pf_bf16* q, int64_t n_q, int n_heads,
                           int32_t* ids_out, float* scores_out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Sub-sampled scoring: the same score computed from query rows 0, q_step,
+ * 2*q_step, ... and heads 0, head_step, 2*head_step, ... only. The pages speed
+ * selection up by scoring with part of the queries and half of the heads
+ * [arXiv HTML, "Implementation Details"]; q_step = head_step = 1 is
+ * pf_score_select. The means run over the rows and heads that are used.
+ * Limits as pf_score_select, plus q_step >= 1 and 1 <= head_step <= n_heads. */
+size_t pf_score_select_sub_workspace_bytes(int64_t n_q, int n_heads, int q_step, int head_step, int n_blocks,
+                                           int n_c);
+
+pf_status pf_score_select_sub(const pf_bf16* q, int64_t n_q, int n_heads, int q_step, int head_step,
+                              const pf_bf16* pool_k, int n_blocks, int n_c, int top_k,
+                              int32_t* ids_out, float* scores_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Batched form: n_batch independent caches (for example the same layer of
  * several videos, or layers whose queries are already known) in one launch
  * sequence. Cache b reads q + b*q_batch_stride and pool_k + b*pool_batch_stride

@@ -170,11 +170,17 @@ def rope_shift_blocks(pool_k_bits: np.ndarray, n_c: int, block_ids: Sequence[int
 # Tokens", "Implementation Details" (N_top = 16)
 # ---------------------------------------------------------------------------
 
-def block_scores(q_bits: np.ndarray, pool_k_bits: np.ndarray, n_c: int) -> np.ndarray:
-    """s_j = (1/H) sum_h <mean_i q_{i,h}, mean_{t in block j} k_{t,h}> / sqrt(128)."""
-    q = bf16_to_f64(q_bits)                       # [n_q, H, D]
+def block_scores(q_bits: np.ndarray, pool_k_bits: np.ndarray, n_c: int, q_step: int = 1,
+                 head_step: int = 1) -> np.ndarray:
+    """s_j = (1/H) sum_h <mean_i q_{i,h}, mean_{t in block j} k_{t,h}> / sqrt(128).
+
+    q_step / head_step > 1: the pages' faster selection ([arXiv] "Implementation
+    Details"): only query rows 0, q_step, ... and heads 0, head_step, ... enter,
+    and the means run over those.
+    """
+    q = bf16_to_f64(q_bits)[::q_step, ::head_step]          # [n_q', H', D]
     H = q.shape[1]
-    k = bf16_to_f64(pool_k_bits).reshape(-1, n_c, H, HEAD_DIM)
+    k = bf16_to_f64(pool_k_bits)[:, ::head_step].reshape(-1, n_c, H, HEAD_DIM)
     q_mean = q.mean(axis=0)                       # [H, D]
     k_mean = k.mean(axis=1)                       # [M, H, D]
     per_head = np.einsum("hd,mhd->mh", q_mean, k_mean) / math.sqrt(HEAD_DIM)

@@ -145,3 +145,25 @@ def test_select_batched_equals_single_calls():
                                                                               cfg.block_frames), fr, cfg.block_frames)
         assert d[b].tolist() == d_ref.tolist()
         assert tags[b].cpu().numpy().tolist() == t_ref.tolist()
+
+
+@pytest.mark.parametrize("steps", [(1, 1), (4, 2), (3, 5), (7, 1)])
+def test_select_subsampled(steps):
+    q_step, head_step = steps
+    say(f"test_select_subsampled q_step={q_step} head_step={head_step}")
+    cfg = pfgen.C2Q
+    c = pfgen.make(cfg)
+    ref_s = O.block_scores(c["q"], c["pool_k"], cfg.n_c, q_step=q_step, head_step=head_step)
+    ids, s = pf.pf_score_select_sub(dev(c["q"]), dev(c["pool_k"]), cfg.n_c, cfg.top_k, q_step, head_step)
+    ids, s = ids.cpu().numpy().tolist(), s.cpu().numpy().astype(np.float64)
+    err = float(np.max(np.abs(s - ref_s)))
+    gap = O.topk_gap(ref_s, cfg.top_k)
+    say(f"  score max-abs err {err:.2e}, k/k+1 gap {gap:.3e}")
+    assert err <= 1e-5 + 1e-5 * float(np.max(np.abs(ref_s)))
+    if gap >= FLAG_GAP:
+        assert ids == O.select_topk(ref_s, cfg.top_k)
+    else:
+        assert O.topk_acceptable(ids, ref_s, cfg.top_k, FLAG_GAP)
+    if steps == (1, 1):
+        i1, s1 = _select(c, cfg.n_c, cfg.top_k)
+        assert ids == i1 and np.array_equal(s.astype(np.float32).view(np.uint32), s1.astype(np.float32).view(np.uint32))

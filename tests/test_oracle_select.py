@@ -126,3 +126,21 @@ def test_rollin_block_needs_no_shift_when_selected_last():
     assert d[-1] == 0 and t[M] == fr
     d_ref, _ = O.placement_deltas([1, 4], tags, fr, Bf)
     assert d[:2].tolist() == d_ref.tolist()
+
+
+def test_subsampled_scores_closed_forms():
+    # queries repeated in runs of s rows: every s-th row has the same mean, so
+    # the sub-sampled score equals the full one; odd heads all zero: the
+    # half-heads score is exactly twice the full one (mean over half the heads)
+    rng = np.random.default_rng(9)
+    H, n_c, M, s = 4, 3, 5, 4
+    base = rng.standard_normal((6, H, 128))
+    q = O.f64_to_bf16(np.repeat(base, s, axis=0))
+    pk = O.f64_to_bf16(rng.standard_normal((M * n_c, H, 128)))
+    full = O.block_scores(q, pk, n_c)
+    assert np.allclose(O.block_scores(q, pk, n_c, q_step=s), full, rtol=1e-12, atol=1e-15)
+    q2 = O.bf16_to_f64(q).copy()
+    q2[:, 1::2] = 0.0
+    q2 = O.f64_to_bf16(q2)
+    assert np.allclose(O.block_scores(q2, pk, n_c, head_step=2), 2 * O.block_scores(q2, pk, n_c), rtol=1e-12,
+                       atol=1e-15)
