@@ -210,6 +210,46 @@ def selection_cadence(pf, torch, pfgen, dev, ms_attn, caches=8):
             "full_over_attention": round(float(np.median(t_full)) / ms_attn, 4)}
 
 
+def rollin_overlap(pf, torch, pfgen, step_attn, layers=30, reps=10):
+    """The dual-resolution roll-in of every layer's new compressed block (one
+    batched call) on a second stream, overlapped with a layer's attention on
+    the launch stream: attention time alone, roll-in alone, and both."""
+    cfg = pfgen.C2
+    H, n_c = cfg.heads, cfg.n_c
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed + 7)
+    blk = (torch.randn((2, layers, n_c, H, 128), generator=g, device="cuda") * cfg.scale).to(torch.bfloat16)
+    pool = torch.zeros((2, layers, 2 * n_c, H, 128), dtype=torch.bfloat16, device="cuda")
+    tags = torch.zeros((layers, 2), dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    roll = lambda: pf.pf_rollin_batched(pool[0], pool[1], tags, 1, blk[0], blk[1], 0, stream=side)
+
+    def timed(fn, stream):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    attn_ms = timed(step_attn, main)
+    roll_ms = timed(roll, side)
+
+    def both():
+        side.wait_stream(main)
+        roll()
+        step_attn()
+        main.wait_stream(side)
+    both_ms = timed(both, main)
+    return {"workload": f"{layers} compressed {n_c}-row blocks rolled in on a second stream during one "
+                        f"default layer-step attention",
+            "attn_ms": round(attn_ms, 4), "rollin_ms": round(roll_ms, 4), "attn_with_rollin_ms": round(both_ms, 4)}
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -332,6 +372,9 @@ def main():
         "input_gen_s": round(t_gen, 2),
     }
     out["selection_cadence"] = selection_cadence(pf, torch, pfgen, dev, ms_attn)
+    out["rollin_overlap"] = rollin_overlap(pf, torch, pfgen, step_attn=lambda: pf.pf_partition_attn(
+        t["q"], t["sink_k"], t["sink_v"], t["pool_k"], t["pool_v"], cfg.n_c, ids, t["recent_k"], t["recent_v"],
+        t["cur_k"], t["cur_v"], o=o))
     if not args.no_batched:
         hb = hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, 5)
         # one generation step = layers x denoising steps layer-steps; the eviction

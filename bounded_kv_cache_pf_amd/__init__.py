@@ -43,6 +43,8 @@ _SIGNATURES = {
                                 _i32),
     "pf_selection_deltas_batched": ([_p, _i32, _p, _i32, ctypes.c_int32, ctypes.c_int32, _i32, _p, _p], _i32),
     "pf_rope_shift_batched": ([_p, _i64, _i32, _i64, _i64, _p, _p, _i32, _i32, ctypes.c_double, _p], _i32),
+    "pf_rollin": ([_p, _p, _p, _i32, _i32, _i32, _p, _p, ctypes.c_int32, _p], _i32),
+    "pf_rollin_batched": ([_p, _p, _i64, _p, _i32, _i32, _i32, _i32, _p, _p, _i64, ctypes.c_int32, _i32, _p], _i32),
     "pf_partition_attn_workspace_bytes": ([_i64, _i32, _i64], _sz),
     "pf_partition_attn": ([_p, _i64, _i32,
                            _p, _p, _i64,
@@ -273,6 +275,43 @@ def pf_rope_shift_batched(k, rows_per_block: int, deltas, block_ids=None, rope_b
                                      _ptr(block_ids), _ptr(deltas), n_shift, nb, rope_base, _stream(stream)),
            "pf_rope_shift_batched")
     return k
+
+
+def pf_rollin(pool_k, pool_v, pos_tags, slot: int, block_k, block_v, first_frame: int, stream=None):
+    """Copy one compressed block into pool slot `slot` and set its position tag."""
+    heads = int(pool_k.shape[1])
+    n_c = _kv_rows(block_k, heads, "block_k")
+    if _kv_rows(block_v, heads, "block_v") != n_c:
+        raise ValueError("block_k and block_v differ in rows")
+    rows = _kv_rows(pool_k, heads, "pool_k")
+    if _kv_rows(pool_v, heads, "pool_v") != rows or (slot + 1) * n_c > rows:
+        raise ValueError("pool_k/pool_v must match and hold the slot")
+    _i32_vec(pos_tags, "pos_tags")
+    if pos_tags is not None and pos_tags.numel() <= slot:
+        raise ValueError("pos_tags has no entry for the slot")
+    _check(lib.pf_rollin(_ptr(pool_k), _ptr(pool_v), _ptr(pos_tags), heads, n_c, slot, _ptr(block_k), _ptr(block_v),
+                         first_frame, _stream(stream)), "pf_rollin")
+
+
+def pf_rollin_batched(pool_k, pool_v, pos_tags, slot: int, block_k, block_v, first_frame: int, stream=None):
+    """Roll-in over a batch: pool_k/v [B][rows][H][128] (caches contiguous), pos_tags int32[B][cap],
+    block_k/v [B][n_c][H][128]."""
+    nb, rows, heads, p_stride = _batched_rows(pool_k, "pool_k")
+    nb2, rows2, _, _ = _batched_rows(pool_v, "pool_v")
+    nb3, n_c, _, b_stride = _batched_rows(block_k, "block_k")
+    if nb2 != nb or nb3 != nb or rows2 != rows or (slot + 1) * n_c > rows:
+        raise ValueError("pool and block batches must match and the pool must hold the slot")
+    if pool_v.stride(0) != p_stride or block_v.stride(0) != b_stride:
+        raise ValueError("K and V tensors must have the same batch strides")
+    _i32_vec(pos_tags, "pos_tags")
+    t_stride = 0
+    if pos_tags is not None:
+        if pos_tags.dim() != 2 or pos_tags.shape[0] != nb or pos_tags.shape[1] <= slot:
+            raise ValueError("pos_tags must be [batch][capacity] with room for the slot")
+        t_stride = int(pos_tags.stride(0))
+    _check(lib.pf_rollin_batched(_ptr(pool_k), _ptr(pool_v), p_stride, _ptr(pos_tags), t_stride, heads, n_c, slot,
+                                 _ptr(block_k), _ptr(block_v), b_stride, first_frame, nb, _stream(stream)),
+           "pf_rollin_batched")
 
 
 def pf_partition_attn(q, sink_k, sink_v, pool_k, pool_v, n_c: int, mid_ids, recent_k, recent_v, cur_k, cur_v,

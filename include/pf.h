@@ -240,6 +240,29 @@ pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_heads,
                             float scale, pf_bf16* o, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------- *
+ * Roll-in of a compressed block into the mid pool
+ * [PackForcing arXiv HTML, "Dual-Resolution Shifting Mechanism": when a block
+ *  leaves the recent window its reduced-resolution backup joins the mid buffer]
+ *
+ * Copies block_k/block_v ([n_c][n_heads][128]) into pool rows
+ * slot*n_c .. slot*n_c + n_c - 1 and sets pos_tags[slot] = first_frame (the
+ * frame the block's keys start at; pos_tags may be NULL). The pool must have
+ * room for the slot; nothing else is touched, so the call can run on a stream
+ * of its own while attention reads the other slots.
+ * Batched form: cache b uses pool_k/v + b*pool_batch_stride, pos_tags +
+ * b*tags_batch_stride and block_k/v + b*block_batch_stride (ignored when
+ * n_batch == 1). Limits: 1 <= n_heads <= PF_MAX_HEADS, n_c >= 1, slot >= 0,
+ * 1 <= n_batch <= PF_MAX_BATCH.
+ * ------------------------------------------------------------------------- */
+pf_status pf_rollin(pf_bf16* pool_k, pf_bf16* pool_v, int32_t* pos_tags, int n_heads, int n_c, int slot,
+                    const pf_bf16* block_k, const pf_bf16* block_v, int32_t first_frame, void* stream);
+
+pf_status pf_rollin_batched(pf_bf16* pool_k, pf_bf16* pool_v, int64_t pool_batch_stride,
+                            int32_t* pos_tags, int tags_batch_stride, int n_heads, int n_c, int slot,
+                            const pf_bf16* block_k, const pf_bf16* block_v, int64_t block_batch_stride,
+                            int32_t first_frame, int n_batch, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

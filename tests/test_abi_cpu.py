@@ -112,6 +112,17 @@ def test_batched_validation(pf):
     assert name == "PF_ERR_SHAPE" and "k_batch_stride" in msg
 
 
+def test_rollin_validation(pf):
+    L = pf.lib
+    assert _err(pf, L.pf_rollin(None, B, C, 12, 182, 40, A, B, 0, None))[0] == "PF_ERR_NULL"
+    assert _err(pf, L.pf_rollin(A, B, C, 40, 182, 40, A, B, 0, None))[0] == "PF_ERR_UNSUPPORTED"
+    assert _err(pf, L.pf_rollin(A, B, C, 12, 182, -1, A, B, 0, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_rollin(A + 8, B, C, 12, 182, 4, A, B, 0, None))[0] == "PF_ERR_MISALIGNED"
+    blk = 182 * 12 * 128
+    name, msg = _err(pf, L.pf_rollin_batched(A, B, 40 * blk, C, 41, 12, 182, 40, A, B, blk, 0, 30, None))
+    assert name == "PF_ERR_SHAPE" and "slot" in msg
+
+
 def _attn(pf, **kw):
     args = dict(q=A, n_q=6240, H=12, sk=B, sv=C, ns=12480, pk=B, pv=C, nb=40, nc=182, ids=A, nsel=16,
                 rk=B, rv=C, nr=6240, ck=B, cv=C, ncur=6240, scale=0.0, o=A, lse=None, ws=None, wsb=0)

@@ -176,13 +176,47 @@ def test_full_generation_step_c3():
     for step in range(S):
         run_step(step, M, fr)
     # roll-in: the recent block leaves the window and joins the pool compressed
-    for l in range(L):
-        blk = pfgen.rollin_block(cfg, l)
-        pool_k_dev[l, M * n_c:] = dev(blk["k"])
-        pool_v_dev[l, M * n_c:] = dev(blk["v"])
+    blocks = [pfgen.rollin_block(cfg, l) for l in range(L)]
+    tags_dev = torch.cat([tags_dev, torch.zeros((L, 1), dtype=torch.int32, device="cuda")], dim=1).contiguous()
+    pf.pf_rollin_batched(pool_k_dev, pool_v_dev, tags_dev, M, dev(np.stack([b["k"] for b in blocks])),
+                         dev(np.stack([b["v"] for b in blocks])), fr)
+    for l, blk in enumerate(blocks):
         ref_pool_k[l], ref_pool_v[l], ref_tags[l] = O.rollin(ref_pool_k[l], ref_pool_v[l], ref_tags[l], blk["k"],
                                                              blk["v"], fr)
-    tags_dev = torch.cat([tags_dev, torch.full((L, 1), fr, dtype=torch.int32, device="cuda")], dim=1).contiguous()
+    assert tags_dev.cpu().numpy().tolist() == [t.tolist() for t in ref_tags]
+    assert np.array_equal(host(pool_v_dev[:, M * n_c:]), np.stack([b["v"] for b in blocks]))
     say("  rolled in one block per layer")
     run_step(S, M + 1, fr + Bf)
     assert len(diverged) <= 2
+
+
+def test_rollin_on_a_second_stream_during_attention():
+    """The roll-in writes the slot after the pool's last block on its own stream
+    while attention reads the earlier slots: both results are exact."""
+    say("test_rollin_on_a_second_stream_during_attention")
+    cfg = pfgen.C1
+    c = pfgen.make(cfg)
+    M, n_c = cfg.pool_blocks, cfg.n_c
+    t = {k: dev(v) for k, v in c.items() if k != "deltas"}
+    pk = torch.cat([t["pool_k"], torch.zeros_like(t["pool_k"][:n_c])]).contiguous()
+    pv = torch.cat([t["pool_v"], torch.zeros_like(t["pool_v"][:n_c])]).contiguous()
+    tags = dev_i32(np.r_[O.initial_pos_tags(M, cfg.sink_blocks, cfg.block_frames), -1])
+    blk = pfgen.rollin_block(cfg, 0)
+    bk, bv = dev(blk["k"]), dev(blk["v"])
+    ids = dev_i32(list(range(0, 32, 2)))
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    o, _ = pf.pf_partition_attn(t["q"], t["sink_k"], t["sink_v"], pk[:M * n_c], pv[:M * n_c], n_c, ids,
+                                t["recent_k"], t["recent_v"], t["cur_k"], t["cur_v"])
+    with torch.cuda.stream(side):
+        pf.pf_rollin(pk, pv, tags, M, bk, bv, 1234)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(pk[M * n_c:]), blk["k"]) and np.array_equal(host(pv[M * n_c:]), blk["v"])
+    assert np.array_equal(host(pk[:M * n_c]), c["pool_k"])
+    assert tags.cpu().numpy().tolist()[M] == 1234
+    rows = np.r_[0, 1, 1000, cfg.n - 1]
+    ks, vs = O.partitions(c, n_c, list(range(0, 32, 2)))
+    ref, _ = O.attn_partitioned(c["q"][rows], ks, vs)
+    mx, mean, rel = attn_errors(host(o)[rows], ref)
+    say(f"  attention alongside the roll-in: max-abs {mx:.2e} rel-L2 {rel:.2e}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2
