@@ -133,3 +133,50 @@ def test_attn_unbounded_c4_sampled_rows():
     cfg = pfgen.C4
     c = pfgen.make(cfg)
     _compare(c, cfg.n_c, [], rows=_sample_rows(cfg.n, 4, extra=8), label="C4 748,800 keys")
+
+
+def _bits(rng, rows, H, scale=1.0):
+    return O.f64_to_bf16(rng.standard_normal((rows, H, 128)) * scale)
+
+
+@pytest.mark.parametrize("H", [1, 32])
+def test_attn_head_count_limits(H):
+    say(f"test_attn_head_count_limits H={H}")
+    rng = np.random.default_rng(20 + H)
+    n_q = 300 if H == 32 else 1000
+    c = dict(q=_bits(rng, n_q, H), sink_k=_bits(rng, 130, H), sink_v=_bits(rng, 130, H),
+             pool_k=_bits(rng, 6 * 11, H), pool_v=_bits(rng, 6 * 11, H), recent_k=_bits(rng, 70, H),
+             recent_v=_bits(rng, 70, H), cur_k=_bits(rng, 90, H), cur_v=_bits(rng, 90, H))
+    _compare(c, 11, [5, 1, 3], rows=_sample_rows(n_q, H), label=f"H={H}")
+
+
+def test_attn_max_selected_blocks_duplicates_and_scale():
+    say("test_attn_max_selected_blocks_duplicates_and_scale")
+    rng = np.random.default_rng(31)
+    H, n_c = 2, 2
+    c = dict(q=_bits(rng, 130, H), sink_k=_bits(rng, 5, H), sink_v=_bits(rng, 5, H),
+             pool_k=_bits(rng, 1200 * n_c, H), pool_v=_bits(rng, 1200 * n_c, H), recent_k=_bits(rng, 3, H),
+             recent_v=_bits(rng, 3, H), cur_k=_bits(rng, 7, H), cur_v=_bits(rng, 7, H))
+    ids = rng.integers(0, 1200, 1024).tolist()          # PF_MAX_SELECTED ids, repeats allowed
+    _compare(c, n_c, ids, label="1024 selected blocks with repeats")
+    o, lse = _run(c, n_c, ids, scale=0.03)
+    ks, vs = O.partitions(c, n_c, ids)
+    # the oracle applies 1/sqrt(128); fold the requested scale into its queries
+    qs = O.f64_to_bf16(O.bf16_to_f64(c["q"]) * (0.03 * np.sqrt(128.0)))
+    ref, _ = O.attn_partitioned(qs, ks, vs)
+    # the scaled queries were rounded to bf16 for the reference: allow that rounding
+    mx, mean, rel = attn_errors(o, ref)
+    say(f"  scale 0.03: max-abs {mx:.2e} rel-L2 {rel:.2e}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2
+
+
+def test_attn_whole_rounds_and_tail_only_plans():
+    # 512 units = exactly the resident workgroups (one round, no tail), and 480
+    # units (no whole round: every unit runs whole in the tail slots)
+    say("test_attn_whole_rounds_and_tail_only_plans")
+    rng = np.random.default_rng(41)
+    for H, n_q in ((32, 2048), (20, 3000)):
+        c = dict(q=_bits(rng, n_q, H, 0.7), sink_k=_bits(rng, 256, H, 0.7), sink_v=_bits(rng, 256, H, 0.7),
+                 pool_k=_bits(rng, 4 * 9, H, 0.7), pool_v=_bits(rng, 4 * 9, H, 0.7), recent_k=_bits(rng, 64, H, 0.7),
+                 recent_v=_bits(rng, 64, H, 0.7), cur_k=_bits(rng, 100, H, 0.7), cur_v=_bits(rng, 100, H, 0.7))
+        _compare(c, 9, [3, 0], rows=_sample_rows(n_q, H, extra=16), label=f"H={H} n_q={n_q}")
