@@ -7,9 +7,12 @@
 // list; nothing is concatenated in memory.
 //
 // Design (gfx950, wave64, bf16 MFMA 32x32x16 with fp32 accumulation):
-//  * A workgroup of 4 waves owns a unit = 128 queries of one head; each wave
-//    owns 32 queries. Two workgroups share a CU (occupancy 2), so one wave's
-//    softmax overlaps the other wave's matrix products on the same SIMD.
+//  * A workgroup of 8 waves owns a unit = 256 queries of one head; each wave
+//    owns 32 queries and two waves share each SIMD, so one wave's softmax
+//    overlaps the other's matrix products. Every K/V tile brought into LDS
+//    feeds 256 queries.
+//  * The MFMA operands read from LDS run kRing-1 MFMAs ahead of their use
+//    (an operand ring), so no MFMA waits on the LDS latency of its own read.
 //  * Keys stream in tiles of 64 straight from global memory into LDS
 //    (global_load_lds, 16 bytes per lane, no register staging), double
 //    buffered. Each 256-byte LDS row holds one key's 128 dims with its 16-byte
@@ -45,11 +48,13 @@ using pf::floatx16;
 using pf::short4v;
 
 constexpr int D = PF_HEAD_DIM;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;         // queries per unit
 constexpr int kBN = 64;                  // keys per tile
-constexpr int kOcc = 2;                  // workgroups per CU the kernel is built for
+constexpr int kRowsPerWave = kBN / kWaves;   // tile rows each wave loads
+constexpr int kLoadsPerWave = kRowsPerWave / 4;   // four rows (1 KB) per load instruction
+constexpr int kOcc = 1;                  // workgroups per CU the kernel is built for
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.0f;    // log2 units: p may grow to 2^8 before a rescale
 constexpr int kMinTailTiles = 16;        // shortest run of key tiles worth a partial
@@ -125,8 +130,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Issue the loads of key tile kt (keys kt*64 ..) into LDS buffers ks/vs.
-// Wave w fills rows 16w .. 16w+15, four rows (1 KB) per instruction; lane L
-// lands on row 16w + 4i + L/16 at physical chunk L%16, so it fetches logical
+// Wave w fills rows 8w .. 8w+7, four rows (1 KB) per instruction; lane L
+// lands on row 8w + 4i + L/16 at physical chunk L%16, so it fetches logical
 // chunk (L%16) ^ swz(row). lane_off[i] holds that lane's element offset within
 // a contiguous partition: (L/16) rows plus the logical chunk.
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const int32_t* ids_lds, int h, int32_t kt,
@@ -145,11 +150,11 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const int32_t* ids
     kbase = a.k_cur; vbase = a.v_cur; r0 = k0 - a.e_rec;
   }
   if (kbase != nullptr) {
-    const int64_t off0 = (static_cast<int64_t>(r0) + 16 * wave_u) * a.row_stride + h * D;
+    const int64_t off0 = (static_cast<int64_t>(r0) + kRowsPerWave * wave_u) * a.row_stride + h * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kLoadsPerWave; ++i) {
       const int64_t off = off0 + 4 * i * a.row_stride;
-      const int lds_row = 16 * wave_u + 4 * i;
+      const int lds_row = kRowsPerWave * wave_u + 4 * i;
       __builtin_amdgcn_global_load_lds(kbase + off + lane_off[i], (lds_void*)(ks + lds_row * D), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vbase + off + lane_off[i], (lds_void*)(vs + lds_row * D), 16, 0, 0);
     }
@@ -158,13 +163,13 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const int32_t* ids
   // general path: resolve each row (mid blocks through the ids, masked rows)
   const int pchunk = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * wave_u + 4 * i + (lane >> 4);
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int row = kRowsPerWave * wave_u + 4 * i + (lane >> 4);
     const uint16_t* kp;
     const uint16_t* vp;
     const bool ok = resolve_key(a, ids_lds, k0 + row, kp, vp);
     const int off = h * D + ((pchunk ^ swz(row)) << 3);
-    const int lds_row = 16 * wave_u + 4 * i;
+    const int lds_row = kRowsPerWave * wave_u + 4 * i;
     __builtin_amdgcn_global_load_lds(kp + off, (lds_void*)(ks + lds_row * D), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(vp + off, (lds_void*)(vs + lds_row * D), 16, 0, 0);
     if (pchunk == 0) kbad[row] = ok ? 0 : 1;
@@ -185,6 +190,26 @@ __device__ __forceinline__ short4v lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
 }
 
+// Operand ring of a run of N MFMAs whose operands take RPO LDS reads each:
+// keep the reads of the first kRing-1 operands, then MFMA i followed by the
+// reads of operand i+kRing-1, in that order in the final schedule.
+constexpr int kRing = 3;
+
+template <int N, int RPO, int I>
+__device__ __forceinline__ void sched_ring_step() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I + kRing - 1 < N) __builtin_amdgcn_sched_group_barrier(0x100, RPO, 0);
+    sched_ring_step<N, RPO, I + 1>();
+  }
+}
+
+template <int N, int RPO>
+__device__ __forceinline__ void sched_ring() {
+  __builtin_amdgcn_sched_group_barrier(0x100, (kRing - 1) * RPO, 0);
+  sched_ring_step<N, RPO, 0>();
+}
+
 struct Smem {
   uint16_t ks[2][kBN * D];
   uint16_t vs[2][kBN * D];
@@ -193,7 +218,7 @@ struct Smem {
   int any_bad_id;
 };
 
-// One unit (head h, queries q0 .. q0+127) over key tiles [kt0, kt1).
+// One unit (head h, queries q0 .. q0+kBM-1) over key tiles [kt0, kt1).
 // direct: the run covers the whole unit -> write O (and LSE); otherwise write
 // the unnormalised partial U, m (log2 domain) and l to partial slot `slot`.
 __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int64_t q0, int kt0, int kt1,
@@ -242,10 +267,11 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
     v_hi[db] = (v_r + 8) * D + (((4 * db + v_x) ^ swz(v_r + 8)) << 3) + v_h;
   }
   // tile loader: element offset of this lane inside a contiguous partition
-  int lane_off[4];
+  int lane_off[kLoadsPerWave];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    lane_off[i] = static_cast<int>((lane >> 4) * a.row_stride) + (((lane & 15) ^ swz(4 * i + (lane >> 4))) << 3);
+  for (int i = 0; i < kLoadsPerWave; ++i)
+    lane_off[i] = static_cast<int>((lane >> 4) * a.row_stride) +
+                  (((lane & 15) ^ swz(kRowsPerWave * wave + 4 * i + (lane >> 4))) << 3);
 
   issue_tile(a, sm.ids, h, kt0, sm.ks[0], sm.vs[0], sm.kbad[0], wave_u, lane, lane_off);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -263,15 +289,21 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
     const uint16_t* vt_lds = sm.vs[buf];
 
     // ---- S^T = K Q^T for two 32-key blocks ----
+    // operand i: dims 16st.. (st = i/2) of key block kb = i%2, so the two
+    // accumulator chains alternate; operand i+kRing-1 is read while MFMA i issues
     floatx16 s[2];
+    {
+      auto load_k = [&](int i) { return *reinterpret_cast<const bf16x8*>(kt_lds + (i & 1) * 32 * D + k_off[i >> 1]); };
+      bf16x8 op[kRing];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = floatx16{};
+      for (int r = 0; r < kRing - 1; ++r) op[r] = load_k(r);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt_lds + kb * 32 * D + k_off[st]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[kb], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        if (i + kRing - 1 < 16) op[(i + kRing - 1) % kRing] = load_k(i + kRing - 1);
+        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % kRing], qf[i >> 1], i < 2 ? floatx16{} : s[i & 1],
+                                                           0, 0, 0);
       }
+      sched_ring<16, 1>();
     }
 
     // ---- mask keys that do not exist ----
@@ -324,15 +356,22 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
       for (int t = 0; t < 8; ++t) pb[c][t] = static_cast<__bf16>(s[c >> 1][8 * (c & 1) + t]);
 
     // ---- O^T += V^T P^T ----
+    // operand i: keys 16c.. (c = i/4), dims 32db.. (db = i%4): four chains
+    {
+      auto load_v = [&](int i) {
+        const short4v lo = lds_read_tr(vt_lds + 16 * (i >> 2) * D + v_lo[i & 3]);
+        const short4v hi = lds_read_tr(vt_lds + 16 * (i >> 2) * D + v_hi[i & 3]);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 op[kRing];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+      for (int r = 0; r < kRing - 1; ++r) op[r] = load_v(r);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const short4v lo = lds_read_tr(vt_lds + 16 * c * D + v_lo[db]);
-        const short4v hi = lds_read_tr(vt_lds + 16 * c * D + v_hi[db]);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], acc[db], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        if (i + kRing - 1 < 16) op[(i + kRing - 1) % kRing] = load_v(i + kRing - 1);
+        acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % kRing], pb[i >> 2], acc[i & 3], 0, 0, 0);
       }
+      sched_ring<16, 2>();
     }
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -360,7 +399,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
             l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
   } else {
-    // partial slot: U [128 queries][128 dims], then m [128], l [128]
+    // partial slot: U [256 queries][128 dims], then m [256], l [256]
     float* base = a.part + slot * static_cast<int64_t>(kPartFloats);
     const int ql = wave * 32 + l32;
     float* up = base + static_cast<int64_t>(ql) * D;

@@ -40,7 +40,7 @@ def _compare(c, n_c, ids, rows=None, label=""):
 
 def _sample_rows(n_q, seed=0, extra=48):
     rng = np.random.default_rng(seed)
-    fixed = [0, 1, 31, 32, 63, 64, 127, 128, n_q // 2, n_q - 97, n_q - 96, n_q - 33, n_q - 32, n_q - 1]
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 257, n_q // 2, n_q - 97, n_q - 96, n_q - 33, n_q - 32, n_q - 1]
     rows = set(r for r in fixed if 0 <= r < n_q) | set(rng.integers(0, n_q, extra).tolist())
     return np.array(sorted(rows))
 
@@ -171,7 +171,7 @@ def test_attn_max_selected_blocks_duplicates_and_scale():
 
 
 def test_attn_whole_rounds_and_tail_only_plans():
-    # 512 units = exactly the resident workgroups (one round, no tail), and 480
+    # 256 units = exactly the resident workgroups (one round, no tail), and 240
     # units (no whole round: every unit runs whole in the tail slots)
     say("test_attn_whole_rounds_and_tail_only_plans")
     rng = np.random.default_rng(41)
