@@ -13,16 +13,16 @@
 //    feeds 256 queries.
 //  * The MFMA operands read from LDS run kRing-1 MFMAs ahead of their use
 //    (an operand ring), so no MFMA waits on the LDS latency of its own read.
-//  * Keys stream in tiles of 64 straight from global memory into LDS
+//  * Keys stream in tiles of 128 straight from global memory into LDS
 //    (global_load_lds, 16 bytes per lane, no register staging), double
 //    buffered. Each 256-byte LDS row holds one key's 128 dims with its 16-byte
 //    chunks XOR-swizzled by the row, so the K reads (16 bytes per lane) and the
 //    transposing V reads (8 bytes per lane) hit distinct banks. Tiles inside a
 //    contiguous partition take a uniform fast path; tiles in the mid blocks or
 //    at the end resolve each row.
-//  * The score tile is computed transposed, S^T = K Q^T, so each lane holds one
-//    query's 32 scores: the row max needs one swap between half-waves, the row
-//    sum none, and the probabilities are already in the B-operand layout of
+//  * The score tile is computed transposed, S^T = K Q^T, so each lane holds
+//    half of one query's 128 scores and the other half-wave the rest: the row
+//    max needs one swap between half-waves, the row sum none, and the probabilities are already in the B-operand layout of
 //    O^T = V^T P^T. V is read with the gfx950 transposing LDS read.
 //  * Online softmax in the log2 domain. The running max is only raised when a
 //    tile's max exceeds it by more than 2^8, so the O rescale (a wave-uniform
@@ -51,7 +51,8 @@ constexpr int D = PF_HEAD_DIM;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;         // queries per unit
-constexpr int kBN = 64;                  // keys per tile
+constexpr int kBN = 128;                 // keys per tile
+constexpr int kNB = kBN / 32;            // 32-key blocks per tile
 constexpr int kRowsPerWave = kBN / kWaves;   // tile rows each wave loads
 constexpr int kLoadsPerWave = kRowsPerWave / 4;   // four rows (1 KB) per load instruction
 constexpr int kOcc = 1;                  // workgroups per CU the kernel is built for
@@ -129,9 +130,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // transposing V read lands on 16 distinct chunks as well.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// Issue the loads of key tile kt (keys kt*64 ..) into LDS buffers ks/vs.
-// Wave w fills rows 8w .. 8w+7, four rows (1 KB) per instruction; lane L
-// lands on row 8w + 4i + L/16 at physical chunk L%16, so it fetches logical
+// Issue the loads of key tile kt (keys kt*kBN ..) into LDS buffers ks/vs.
+// Wave w fills rows 16w .. 16w+15, four rows (1 KB) per instruction; lane L
+// lands on row 16w + 4i + L/16 at physical chunk L%16, so it fetches logical
 // chunk (L%16) ^ swz(row). lane_off[i] holds that lane's element offset within
 // a contiguous partition: (L/16) rows plus the logical chunk.
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const int32_t* ids_lds, int h, int32_t kt,
@@ -288,29 +289,29 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
     const uint16_t* kt_lds = sm.ks[buf];
     const uint16_t* vt_lds = sm.vs[buf];
 
-    // ---- S^T = K Q^T for two 32-key blocks ----
-    // operand i: dims 16st.. (st = i/2) of key block kb = i%2, so the two
+    // ---- S^T = K Q^T for kNB 32-key blocks ----
+    // operand i: dims 16st.. (st = i/kNB) of key block kb = i%kNB, so the kNB
     // accumulator chains alternate; operand i+kRing-1 is read while MFMA i issues
-    floatx16 s[2];
+    floatx16 s[kNB];
     {
-      auto load_k = [&](int i) { return *reinterpret_cast<const bf16x8*>(kt_lds + (i & 1) * 32 * D + k_off[i >> 1]); };
+      auto load_k = [&](int i) { return *reinterpret_cast<const bf16x8*>(kt_lds + (i % kNB) * 32 * D + k_off[i / kNB]); };
       bf16x8 op[kRing];
 #pragma unroll
       for (int r = 0; r < kRing - 1; ++r) op[r] = load_k(r);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i + kRing - 1 < 16) op[(i + kRing - 1) % kRing] = load_k(i + kRing - 1);
-        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % kRing], qf[i >> 1], i < 2 ? floatx16{} : s[i & 1],
+      for (int i = 0; i < 8 * kNB; ++i) {
+        if (i + kRing - 1 < 8 * kNB) op[(i + kRing - 1) % kRing] = load_k(i + kRing - 1);
+        s[i % kNB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % kRing], qf[i / kNB], i < kNB ? floatx16{} : s[i % kNB],
                                                            0, 0, 0);
       }
-      sched_ring<16, 1>();
+      sched_ring<8 * kNB, 1>();
     }
 
     // ---- mask keys that do not exist ----
     const bool need_mask = (k0 + kBN > a.e_cur) || (bad_ids && k0 < a.e_mid && k0 + kBN > a.e_sink);
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kNB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
@@ -323,7 +324,9 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    for (int kb = 1; kb < kNB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = half_swap_max(mx) * a.scale_log2;
     const bool grow = mx > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -339,7 +342,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kNB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_use));
@@ -349,9 +352,9 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
     l_run += psum;
 
     // ---- P^T as the B operand: chunk c covers keys 16c .. 16c+15 ----
-    bf16x8 pb[4];
+    bf16x8 pb[2 * kNB];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 2 * kNB; ++c)
 #pragma unroll
       for (int t = 0; t < 8; ++t) pb[c][t] = static_cast<__bf16>(s[c >> 1][8 * (c & 1) + t]);
 
@@ -367,11 +370,11 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
 #pragma unroll
       for (int r = 0; r < kRing - 1; ++r) op[r] = load_v(r);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i + kRing - 1 < 16) op[(i + kRing - 1) % kRing] = load_v(i + kRing - 1);
+      for (int i = 0; i < 8 * kNB; ++i) {
+        if (i + kRing - 1 < 8 * kNB) op[(i + kRing - 1) % kRing] = load_v(i + kRing - 1);
         acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % kRing], pb[i >> 2], acc[i & 3], 0, 0, 0);
       }
-      sched_ring<16, 2>();
+      sched_ring<8 * kNB, 2>();
     }
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
