@@ -366,3 +366,75 @@ def layer_step(cache: Dict[str, np.ndarray], pos_tags: np.ndarray, n_c: int, top
     o, lse = attn_partitioned(q, ks, vs)
     return {"scores": scores, "ids": ids, "gap": topk_gap(scores, top_k), "deltas": deltas,
             "tags": tags, "pool_k": pool_k, "o": o, "lse": lse}
+
+
+# ---------------------------------------------------------------------------
+# HR branch of the compressor  [arXiv] "HR Branch: Progressive 3D Convolution"
+# and "Feature Fusion" (N_c = floor(T/2) floor(H/8) floor(W/8)); [digest]
+# 前置知识 3D卷积 and 方法步骤详情 (2)
+# ---------------------------------------------------------------------------
+#
+# Readings where the pages are silent (listed in the design notes):
+#  * each strided convolution has its kernel equal to its stride and no
+#    padding, so every output position sees one disjoint input patch and every
+#    dimension is floored, which is exactly what the N_c formula counts;
+#  * SiLU follows each strided convolution; the final 1x1x1 projection to the
+#    hidden width is linear;
+#  * activations are stored channels-last, [B][T][H][W][C], as bfloat16 after
+#    every stage (round-to-nearest-even of the exact value), the way a bf16
+#    network keeps them; weights are [C_out][kt][kh][kw][C_in] bfloat16 and
+#    biases float32;
+#  * the compressed tokens are numbered t-major: token (t, h, w) is row
+#    (t*H_out + h)*W_out + w.
+
+HR_STAGE_KERNELS = ((2, 1, 1), (1, 2, 2), (1, 2, 2), (1, 2, 2))
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x), written so that neither branch overflows."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, x / (1.0 + e), x * e / (1.0 + e))
+
+
+def hr_conv_stage(x_bits: np.ndarray, w_bits: np.ndarray, bias, kernel, act: bool = True,
+                  round_output: bool = True) -> np.ndarray:
+    """One strided 3D convolution (kernel = stride, no padding) plus bias and,
+    when act, SiLU. x_bits [B][T][H][W][C_in] and w_bits
+    [C_out][kt][kh][kw][C_in] are bfloat16 bits; bias is [C_out] (or None).
+    The output is [B][T//kt][H//kh][W//kw][C_out]: bfloat16 bits, or the exact
+    float64 values when round_output is False."""
+    x = bf16_to_f64(x_bits)
+    kt, kh, kw = kernel
+    B, T, H, W, C = x.shape
+    w = bf16_to_f64(w_bits)
+    c_out = w.shape[0]
+    assert w.shape == (c_out, kt, kh, kw, C), (w.shape, kernel, C)
+    To, Ho, Wo = T // kt, H // kh, W // kw
+    x = x[:, :To * kt, :Ho * kh, :Wo * kw, :]
+    # each output position's patch, flattened in (dt, dh, dw, c) order
+    patches = x.reshape(B, To, kt, Ho, kh, Wo, kw, C).transpose(0, 1, 3, 5, 2, 4, 6, 7)
+    patches = patches.reshape(B * To * Ho * Wo, kt * kh * kw * C)
+    y = patches @ w.reshape(c_out, -1).T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    if act:
+        y = silu(y)
+    y = y.reshape(B, To, Ho, Wo, c_out)
+    return f64_to_bf16(y) if round_output else y
+
+
+def hr_branch(z_bits: np.ndarray, stages, proj) -> np.ndarray:
+    """The HR branch: the strided stages of HR_STAGE_KERNELS, each followed by
+    SiLU, then the linear 1x1x1 projection. z_bits is the latent block
+    [B][T][H][W][C] (bfloat16 bits); stages is a list of (w_bits, bias), one per
+    kernel; proj is (w_bits [d][C_last], bias). Returns [B][N_c][d] bfloat16
+    bits with N_c = (T//2) (H//8) (W//8) tokens numbered t-major."""
+    x = z_bits
+    for (w, b), k in zip(stages, HR_STAGE_KERNELS):
+        x = hr_conv_stage(x, w, b, k, act=True)
+    wp, bp = proj
+    d = wp.shape[0]
+    y = hr_conv_stage(x, wp.reshape(d, 1, 1, 1, -1), bp, (1, 1, 1), act=False)
+    B, To, Ho, Wo, _ = y.shape
+    return y.reshape(B, To * Ho * Wo, d)

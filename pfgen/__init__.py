@@ -203,3 +203,49 @@ def planted_pool(cfg: Config, seed: int, chosen: List[int], margin: float = 4.0)
 
 def _from_bits(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# HR-branch compressor inputs: a latent block and synthetic weights
+# ---------------------------------------------------------------------------
+# The latent block is what the VAE yields for one generated block: B_f = 4
+# latent frames of 60 x 104 (the 30 x 52 token grid before the 1x2x2 patch
+# embedding) [PackForcing, arXiv HTML, "HR Branch" and "Feature Fusion"], with
+# 16 latent channels (the base model's VAE; the pages do not print it). The
+# stage widths are this library's reading (the pages give none): 256, 512,
+# 1024, 2048, then the hidden width 1536. Trained weights are not available;
+# these are seeded draws with fan-in scaling, so activations stay of order 1.
+
+HR_LATENT = dict(frames=4, height=60, width=104, channels=16)
+HR_WIDTHS = (256, 512, 1024, 2048)
+HR_HIDDEN = 1536
+HR_KERNELS = ((2, 1, 1), (1, 2, 2), (1, 2, 2), (1, 2, 2))
+
+
+def hr_latent(seed: int, batch: int = 1, frames: int = 4, height: int = 60, width: int = 104,
+              channels: int = 16) -> np.ndarray:
+    """[batch][frames][height][width][channels] standard normals as bf16 bits."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return bf16_bits(rng.standard_normal((batch, frames, height, width, channels), dtype=np.float32))
+
+
+def hr_weights(seed: int, channels: int = 16, widths=HR_WIDTHS, hidden: int = HR_HIDDEN,
+               kernels=HR_KERNELS, bias_std: float = 0.1):
+    """Seeded weights for the strided stages and the projection.
+
+    Returns (stages, proj): stages is a list of (w_bits [C_out][kt][kh][kw][C_in],
+    bias float32 [C_out]); proj is (w_bits [hidden][C_last], bias float32).
+    Each weight is N(0, 2/fan_in), each bias N(0, bias_std^2).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    stages = []
+    c_in = channels
+    for c_out, (kt, kh, kw) in zip(widths, kernels):
+        fan_in = kt * kh * kw * c_in
+        w = rng.standard_normal((c_out, kt, kh, kw, c_in), dtype=np.float32) * np.float32(np.sqrt(2.0 / fan_in))
+        b = rng.standard_normal(c_out, dtype=np.float32) * np.float32(bias_std)
+        stages.append((bf16_bits(w), b))
+        c_in = c_out
+    wp = rng.standard_normal((hidden, c_in), dtype=np.float32) * np.float32(np.sqrt(1.0 / c_in))
+    bp = rng.standard_normal(hidden, dtype=np.float32) * np.float32(bias_std)
+    return stages, (bf16_bits(wp), bp)
