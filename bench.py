@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--batched-only", action="store_true",
                     help="only run the batched selection/RoPE measurement (for its own profile)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--hr-only", action="store_true",
+                    help="time only the HR-branch compressor (for profiling its kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -250,6 +252,81 @@ def rollin_overlap(pf, torch, pfgen, step_attn, layers=30, reps=10):
             "attn_ms": round(attn_ms, 4), "rollin_ms": round(roll_ms, 4), "attn_with_rollin_ms": round(both_ms, 4)}
 
 
+def hr_branch(pf, torch, pfgen, dev, gen_ms, reps=20):
+    """The HR-branch compressor on the default latent block (4 frames of
+    60 x 104 x 16 channels -> 182 tokens x 1536) with seeded weights: the whole
+    branch at batch 1 (one block, as it runs once per generated block) and
+    batch 8, and each strided stage alone at batch 1 with its own roofline
+    (algorithmic flops 2 M N K; bytes = input + weights + bias + output)."""
+    lat = pfgen.HR_LATENT
+    T, H, W, C = lat["frames"], lat["height"], lat["width"], lat["channels"]
+    stages, (wp, bp) = pfgen.hr_weights(3001)
+    ds = [(dev(w), torch.from_numpy(b).cuda()) for w, b in stages]
+    dp = (dev(wp), torch.from_numpy(bp).cuda())
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        # these launches are shorter than the host cost of a call, so the reps
+        # are captured once in a HIP graph and the graph's replay is timed
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(reps):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {"workload": f"HR branch on {T}x{H}x{W}x{C} latent blocks, widths {list(pfgen.HR_WIDTHS)} -> "
+                       f"{pfgen.HR_HIDDEN}, seeded weights"}
+    rows, flops_block = [], 0
+    t, h, w, c = T, H, W, C
+    layers = [(wd, k, True, st) for wd, k, st in zip(pfgen.HR_WIDTHS, pfgen.HR_KERNELS, ds)]
+    layers.append((pfgen.HR_HIDDEN, (1, 1, 1), False, (dp[0].view(pfgen.HR_HIDDEN, 1, 1, 1, -1), dp[1])))
+    for wd, (kt, kh, kw), act, (wt, bt) in layers:
+        x = torch.randn((1, t, h, w, c), device="cuda").to(torch.bfloat16)
+        to, ho, wo = t // kt, h // kh, w // kw
+        M, K = to * ho * wo, kt * kh * kw * c
+        y = torch.empty((1, to, ho, wo, wd), dtype=torch.bfloat16, device="cuda")
+        need = pf.pf_hr_conv_workspace_bytes(1, t, h, w, c, (kt, kh, kw), wd)
+        wsb = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: pf.pf_hr_conv(x, wt, bt, (kt, kh, kw), act=act, y=y, workspace=wsb))
+        fl = 2 * M * wd * K
+        by = (to * kt * ho * kh * wo * kw * c + wd * K + M * wd) * 2 + wd * 4
+        flops_block += fl
+        intensity = fl / by
+        bound = "mfma" if intensity > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+        frac = (fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if bound == "mfma" else (by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+        rows.append({"kernel": f"{kt}x{kh}x{kw}", "c_in": c, "c_out": wd, "M": M, "K": K, "ms": round(ms, 4),
+                     "flops": fl, "bytes": by, "bound": bound, "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "GB/s": round(by / (ms * 1e-3) / 1e9, 1), "frac": round(frac, 4),
+                     "split_k_workspace": need})
+        t, h, w, c = to, ho, wo, wd
+        del x, y, wsb
+    out["stages"] = rows
+    out["flops_per_block"] = flops_block
+    for batch in (1, 8):
+        z = torch.randn((batch, T, H, W, C), device="cuda").to(torch.bfloat16)
+        o = torch.empty((batch, (T // 2) * (H // 8) * (W // 8), pfgen.HR_HIDDEN), dtype=torch.bfloat16, device="cuda")
+        wsb = torch.empty(pf.pf_hr_branch_workspace_bytes(batch, T, H, W, C, pfgen.HR_WIDTHS, pfgen.HR_HIDDEN),
+                          dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: pf.pf_hr_branch(z, ds, dp, out=o, workspace=wsb))
+        out[f"batch{batch}_ms"] = round(ms, 4)
+        out[f"batch{batch}_tflops"] = round(batch * flops_block / (ms * 1e-3) / 1e12, 1)
+        del z, o, wsb
+    # the branch runs once per generated block, whose generation takes
+    # layers x denoising steps layer-steps
+    out["frac_of_generation_step"] = round(out["batch1_ms"] / gen_ms, 6)
+    return out
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -278,6 +355,12 @@ def main():
 
     if args.batched_only:
         print(json.dumps({"hbm_batched": hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, args.steps)}), flush=True)
+        return
+    if args.hr_only:
+        def dev_bits(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+        print(json.dumps({"hr_branch": hr_branch(pf, torch, pfgen, dev_bits, gen_ms=float("nan"),
+                                                 reps=args.steps)}), flush=True)
         return
 
     cfg = pfgen.C1
@@ -375,6 +458,7 @@ def main():
     out["rollin_overlap"] = rollin_overlap(pf, torch, pfgen, step_attn=lambda: pf.pf_partition_attn(
         t["q"], t["sink_k"], t["sink_v"], t["pool_k"], t["pool_v"], cfg.n_c, ids, t["recent_k"], t["recent_v"],
         t["cur_k"], t["cur_v"], o=o))
+    out["hr_branch"] = hr_branch(pf, torch, pfgen, dev, gen_ms=pfgen.C3.layers * pfgen.C3.steps * ms_step)
     if not args.no_batched:
         hb = hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, 5)
         # one generation step = layers x denoising steps layer-steps; the eviction

@@ -45,6 +45,10 @@ _SIGNATURES = {
     "pf_rope_shift_batched": ([_p, _i64, _i32, _i64, _i64, _p, _p, _i32, _i32, ctypes.c_double, _p], _i32),
     "pf_rollin": ([_p, _p, _p, _i32, _i32, _i32, _p, _p, ctypes.c_int32, _p], _i32),
     "pf_rollin_batched": ([_p, _p, _i64, _p, _i32, _i32, _i32, _i32, _p, _p, _i64, ctypes.c_int32, _i32, _p], _i32),
+    "pf_hr_conv_workspace_bytes": ([_i32] * 9, _sz),
+    "pf_hr_conv": ([_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32, _i32, _p, _p, _sz, _p], _i32),
+    "pf_hr_branch_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _p, _i32], _sz),
+    "pf_hr_branch": ([_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i32, _p, _p, _sz, _p], _i32),
     "pf_partition_attn_workspace_bytes": ([_i64, _i32, _i64], _sz),
     "pf_partition_attn": ([_p, _i64, _i32,
                            _p, _p, _i64,
@@ -352,3 +356,100 @@ def pf_partition_attn(q, sink_k, sink_v, pool_k, pool_v, n_c: int, mid_ids, rece
                                  float(scale), _ptr(o), _ptr(lse), _ptr(ws), need, _stream(stream)),
            "pf_partition_attn")
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# HR branch of the compressor
+# ---------------------------------------------------------------------------
+
+HR_STAGES = 4
+
+
+def _act5(t, what: str) -> Tuple[int, int, int, int, int]:
+    """A contiguous channels-last bf16 activation [B][T][H][W][C] on the GPU."""
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16):
+        raise TypeError(f"{what} must be bfloat16 (or int16 bf16 bits), got {t.dtype}")
+    if t.dim() != 5 or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous [B][T][H][W][C] tensor, got {tuple(t.shape)}")
+    return tuple(int(v) for v in t.shape)
+
+
+def _f32_vec(t, n: int, what: str) -> None:
+    torch = _torch()
+    if t is None:
+        return
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+        raise TypeError(f"{what} must be a contiguous float32 CUDA tensor of {n} values")
+
+
+def pf_hr_conv_workspace_bytes(n_batch: int, T: int, H: int, W: int, c_in: int, kernel, c_out: int) -> int:
+    kt, kh, kw = kernel
+    return int(lib.pf_hr_conv_workspace_bytes(n_batch, T, H, W, c_in, kt, kh, kw, c_out))
+
+
+def pf_hr_conv(x, w, bias, kernel, act: bool = True, y=None, workspace=None, stream=None):
+    """One strided 3D convolution (kernel = stride) plus bias and SiLU.
+    x [B][T][H][W][C_in], w [C_out][kt][kh][kw][C_in] (bf16 bits), bias fp32 [C_out] or None."""
+    torch = _torch()
+    B, T, H, W, c_in = _act5(x, "x")
+    kt, kh, kw = kernel
+    c_out = int(w.shape[0])
+    if tuple(w.shape) != (c_out, kt, kh, kw, c_in) or not w.is_contiguous() or not w.is_cuda:
+        raise ValueError(f"w must be a contiguous [{c_out}][{kt}][{kh}][{kw}][{c_in}] CUDA tensor")
+    _f32_vec(bias, c_out, "bias")
+    shape = (B, T // kt, H // kh, W // kw, c_out)
+    if y is None:
+        y = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(y.shape) != shape or not y.is_contiguous():
+        raise ValueError(f"y must be a contiguous {shape} tensor")
+    need = pf_hr_conv_workspace_bytes(B, T, H, W, c_in, kernel, c_out)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib.pf_hr_conv(_ptr(x), B, T, H, W, c_in, kt, kh, kw, _ptr(w), _ptr(bias), c_out, 1 if act else 0,
+                          _ptr(y), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                          _stream(stream)), "pf_hr_conv")
+    return y
+
+
+def pf_hr_branch_workspace_bytes(n_batch: int, T: int, H: int, W: int, c_in: int, widths, hidden: int) -> int:
+    wa = (ctypes.c_int * HR_STAGES)(*widths)
+    return int(lib.pf_hr_branch_workspace_bytes(n_batch, T, H, W, c_in, wa, hidden))
+
+
+def pf_hr_branch(z, stages, proj, out=None, workspace=None, stream=None):
+    """The HR branch on a latent block z [B][T][H][W][C]: stages is a list of
+    four (w, bias) pairs (kernels 2x1x1 then 1x2x2 three times, SiLU after
+    each), proj is (w [hidden][C_last], bias). Returns [B][N_c][hidden]."""
+    torch = _torch()
+    B, T, H, W, c_in = _act5(z, "z")
+    if len(stages) != HR_STAGES:
+        raise ValueError(f"stages must hold {HR_STAGES} (weight, bias) pairs")
+    widths = [int(w.shape[0]) for w, _ in stages]
+    keep = []
+    for s, (w, b) in enumerate(stages):
+        if not w.is_cuda or not w.is_contiguous() or w.dim() != 5:
+            raise ValueError(f"stage {s} weight must be a contiguous [C_out][kt][kh][kw][C_in] CUDA tensor")
+        _f32_vec(b, widths[s], f"stage {s} bias")
+        keep += [w, b]
+    wp, bp = proj
+    hidden = int(wp.shape[0])
+    if not wp.is_cuda or not wp.is_contiguous() or wp.dim() != 2 or int(wp.shape[1]) != widths[-1]:
+        raise ValueError(f"proj weight must be a contiguous [hidden][{widths[-1]}] CUDA tensor")
+    _f32_vec(bp, hidden, "proj bias")
+    n_c = (T // 2) * (H // 8) * (W // 8)
+    if out is None:
+        out = torch.empty((B, n_c, hidden), dtype=z.dtype, device=z.device)
+    elif tuple(out.shape) != (B, n_c, hidden) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous ({B}, {n_c}, {hidden}) tensor")
+    need = pf_hr_branch_workspace_bytes(B, T, H, W, c_in, widths, hidden)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=z.device)
+    ws_arr = (ctypes.c_void_p * HR_STAGES)(*[w.data_ptr() for w, _ in stages])
+    bs_arr = (ctypes.c_void_p * HR_STAGES)(*[None if b is None else b.data_ptr() for _, b in stages])
+    wd_arr = (ctypes.c_int * HR_STAGES)(*widths)
+    _check(lib.pf_hr_branch(_ptr(z), B, T, H, W, c_in, ws_arr, bs_arr, wd_arr, _ptr(wp), _ptr(bp), hidden,
+                            _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)), "pf_hr_branch")
+    return out

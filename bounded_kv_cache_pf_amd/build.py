@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpf.so")
-SOURCES = ["pf_status.hip", "pf_rope.hip", "pf_select.hip", "pf_attn.hip", "pf_rollin.hip"]
+SOURCES = ["pf_status.hip", "pf_rope.hip", "pf_select.hip", "pf_attn.hip", "pf_rollin.hip", "pf_hr.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -51,6 +51,7 @@ extern "C" {
 #define PF_MAX_TOPK 256      /* top_k of pf_score_select */
 #define PF_MAX_SELECTED 1024 /* n_sel of pf_partition_attn */
 #define PF_MAX_BATCH 65535   /* n_batch of the _batched calls */
+#define PF_HR_STAGES 4       /* strided stages of the HR branch before the projection */
 
 typedef uint16_t pf_bf16;
 
@@ -262,6 +263,55 @@ pf_status pf_rollin_batched(pf_bf16* pool_k, pf_bf16* pool_v, int64_t pool_batch
                             int32_t* pos_tags, int tags_batch_stride, int n_heads, int n_c, int slot,
                             const pf_bf16* block_k, const pf_bf16* block_v, int64_t block_batch_stride,
                             int32_t first_frame, int n_batch, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * HR branch of the compressor
+ * [PackForcing arXiv HTML, "HR Branch: Progressive 3D Convolution": strided 3D
+ *  convolutions with SiLU halve time once and space three times (2x8x8 =
+ *  128x volume reduction), then a 1x1x1 projection reaches the hidden width;
+ *  "Feature Fusion": N_c = floor(T/2) floor(H/8) floor(W/8) tokens;
+ *  digest (paper.rainbus.top), 前置知识 3D卷积]
+ *
+ * pf_hr_conv: one strided 3D convolution whose kernel equals its stride (no
+ * padding; each output dimension is floor(input / kernel)), plus bias and,
+ * when act != 0, SiLU:
+ *   y[b][t][h][w][n] = act(bias[n] + sum_{dt,dh,dw,c} w[n][dt][dh][dw][c] *
+ *                      x[b][kt*t+dt][kh*h+dh][kw*w+dw][c])
+ * x: [n_batch][T][H][W][c_in] bf16 (channels last); w: [c_out][kt][kh][kw][c_in]
+ * bf16; bias: [c_out] fp32 or NULL; y: [n_batch][T/kt][H/kh][W/kw][c_out] bf16
+ * (round to nearest even of the fp32 result). Accumulation is fp32 in a fixed
+ * order, so results are bit-reproducible. All device pointers, owned by the
+ * caller; x, w, y and workspace 16-byte aligned, bias 4-byte aligned.
+ * Deep stages with few output positions split the reduction and need a
+ * workspace of pf_hr_conv_workspace_bytes(...) bytes (0: none needed; the
+ * size depends on the device's CU count).
+ * Limits: n_batch >= 1; 1 <= kt, kh, kw with kt*kh*kw <= 64 and the input at
+ * least one kernel in every dimension; c_in and c_out multiples of 16 in
+ * [16, 65536]. Errors are returned before anything is enqueued.
+ *
+ * pf_hr_branch: the whole branch on a latent block z [n_batch][T][H][W][c_in]:
+ * stage 0 has kernel 2x1x1, stages 1..3 kernel 1x2x2, each with SiLU and
+ * widths[s] output channels, then the linear projection proj_w
+ * [hidden][widths[3]] (+ proj_b) to out [n_batch][N_c][hidden] with
+ * N_c = (T/2)(H/8)(W/8) tokens numbered t-major. stage_w, stage_b and widths
+ * are HOST arrays of PF_HR_STAGES entries (the weight and bias pointers they
+ * hold are device pointers; stage_b entries may be NULL). The intermediate
+ * activations live in the caller's workspace of
+ * pf_hr_branch_workspace_bytes(...) bytes. Limits: T >= 2, H >= 8, W >= 8 and
+ * those of pf_hr_conv for every stage.
+ * ------------------------------------------------------------------------- */
+size_t pf_hr_conv_workspace_bytes(int n_batch, int T, int H, int W, int c_in, int kt, int kh, int kw, int c_out);
+
+pf_status pf_hr_conv(const pf_bf16* x, int n_batch, int T, int H, int W, int c_in, int kt, int kh, int kw,
+                     const pf_bf16* w, const float* bias, int c_out, int act, pf_bf16* y,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+size_t pf_hr_branch_workspace_bytes(int n_batch, int T, int H, int W, int c_in, const int* widths, int hidden);
+
+pf_status pf_hr_branch(const pf_bf16* z, int n_batch, int T, int H, int W, int c_in,
+                       const pf_bf16* const* stage_w, const float* const* stage_b, const int* widths,
+                       const pf_bf16* proj_w, const float* proj_b, int hidden, pf_bf16* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -162,3 +162,52 @@ def test_binding_rejects_cpu_tensors(pf):
     q = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pf.pf_partition_attn(q, q, q, None, None, 8, None, None, None, q, q)
+
+
+def _conv(pf, **kw):
+    a = dict(x=A, nb=1, T=4, H=60, W=104, ci=16, kt=2, kh=1, kw=1, w=B, b=None, co=256, act=1, y=C, ws=None, wsb=0)
+    a.update(kw)
+    return pf.lib.pf_hr_conv(a["x"], a["nb"], a["T"], a["H"], a["W"], a["ci"], a["kt"], a["kh"], a["kw"], a["w"],
+                             a["b"], a["co"], a["act"], a["y"], a["ws"], a["wsb"], None)
+
+
+def test_hr_conv_validation(pf):
+    assert _err(pf, _conv(pf, x=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, _conv(pf, w=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, _conv(pf, y=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, _conv(pf, x=A + 8))[0] == "PF_ERR_MISALIGNED"
+    assert _err(pf, _conv(pf, b=B + 2))[0] == "PF_ERR_MISALIGNED"
+    assert _err(pf, _conv(pf, nb=0))[0] == "PF_ERR_SHAPE"
+    assert _err(pf, _conv(pf, T=1))[0] == "PF_ERR_SHAPE"            # smaller than the kernel
+    assert _err(pf, _conv(pf, ci=8))[0] == "PF_ERR_UNSUPPORTED"     # not a multiple of 16
+    assert _err(pf, _conv(pf, co=40))[0] == "PF_ERR_UNSUPPORTED"
+    assert _err(pf, _conv(pf, kt=0))[0] == "PF_ERR_UNSUPPORTED"
+    assert _err(pf, _conv(pf, kt=4, kh=4, kw=8, T=8, H=8, W=8))[0] == "PF_ERR_UNSUPPORTED"   # 128 taps
+    # a deep, narrow stage asks for a split-K workspace and refuses to run without it
+    need = pf.lib.pf_hr_conv_workspace_bytes(1, 2, 14, 26, 1024, 1, 2, 2, 2048)
+    assert need > 0
+    name, msg = _err(pf, _conv(pf, T=2, H=14, W=26, ci=1024, kt=1, kh=2, kw=2, co=2048))
+    assert name == "PF_ERR_WORKSPACE" and str(need) in msg
+    # a shallow stage needs none
+    assert pf.lib.pf_hr_conv_workspace_bytes(1, 4, 60, 104, 16, 2, 1, 1, 256) == 0
+
+
+def test_hr_branch_validation(pf):
+    L = pf.lib
+    widths = (ctypes.c_int * 4)(256, 512, 1024, 2048)
+    ws = (ctypes.c_void_p * 4)(B, B, B, B)
+    bs = (ctypes.c_void_p * 4)(None, None, None, None)
+    need = L.pf_hr_branch_workspace_bytes(1, 4, 60, 104, 16, widths, 1536)
+    assert need > 0
+    call = lambda **k: L.pf_hr_branch(k.get("z", A), 1, k.get("T", 4), k.get("H", 60), k.get("W", 104), 16,
+                                      k.get("ws_", ws), bs, k.get("widths", widths), B, None, 1536, C,
+                                      k.get("wsp", A), k.get("wsb", need), None)
+    assert _err(pf, call(z=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, call(ws_=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, call(T=1))[0] == "PF_ERR_SHAPE"
+    assert _err(pf, call(H=7))[0] == "PF_ERR_SHAPE"
+    bad = (ctypes.c_int * 4)(256, 500, 1024, 2048)
+    assert _err(pf, call(widths=bad))[0] == "PF_ERR_UNSUPPORTED"
+    name, msg = _err(pf, call(wsb=need - 1))
+    assert name == "PF_ERR_WORKSPACE" and str(need) in msg
+    assert _err(pf, call(wsp=None))[0] == "PF_ERR_WORKSPACE"
