@@ -18,17 +18,22 @@
 // straight from the activation tensor (an implicit GEMM).
 //
 // Design (gfx950, wave64, MFMA 32x32x16 bf16, fp32 accumulation):
-//  * One wave per workgroup owns 64 output channels x 64 positions (2 x 2
-//    MFMA tiles, the transposed product D^T = W X^T so each lane ends with
-//    four runs of 4 consecutive channels of one position: 8-byte stores).
-//  * Operands come straight from global memory (L2) in the MFMA layout, one
-//    16-byte load per lane per fragment; the next K step's fragments are
-//    loaded while the current step's MFMAs run.
+//  * C_in a multiple of 64 (every stage but the first): a workgroup of 4
+//    waves owns 128 channels x 128 positions. K advances in chunks of 64
+//    elements, one 128-byte run of every weight row and patch row, moved into
+//    LDS by global_load_lds (8 whole rows per instruction, double-buffered,
+//    16-byte chunks XOR-swizzled by row); each wave computes a 64 x 64
+//    sub-tile from LDS fragments.
+//  * Otherwise (the 16-channel latent): one wave per workgroup, operands read
+//    straight from global memory in the MFMA layout, eight K steps in flight.
+//    Its 64 x 64 wave tile drops to 32 x 32 when K is only a few steps deep.
+//  * Both use the transposed product D^T = W X^T and stage the output tile
+//    through LDS, so the stores write whole rows of channels.
 //  * Deep, narrow stages (few positions, K up to 4096) split K over up to 8
 //    workgroups that write fp32 partials; a second kernel sums them in a fixed
 //    order, adds the bias and applies SiLU. Results are bit-reproducible.
-//  * Workgroups are numbered so that the ones sharing a weight slice (same
-//    channel tile and K split) run on the same XCD and share its L2.
+//  * Each XCD gets a contiguous slice of the larger operand (positions or
+//    channels) and all of the smaller, so the smaller stays in its L2.
 #include <math.h>
 
 #include <algorithm>
@@ -44,6 +49,9 @@ constexpr int kMaxSplit = 8;    // K splits of one stage
 constexpr int kXcds = 8;
 constexpr int kTargetWaves = 2048;
 constexpr int kDepth = 8;       // K steps of operands in flight per wave
+// split K only while the fp32 partials written and re-read stay under this
+// multiple of the bytes the stage reads anyway (weights + activations)
+constexpr double kPartialBudget = 2.0;
 
 struct ConvArgs {
   const uint16_t* x;
@@ -237,6 +245,191 @@ __global__ __launch_bounds__(64) void hr_conv_kernel(ConvArgs a) {
   }
 }
 
+// Workgroup-tiled variant for C_in a multiple of 64: a workgroup of 4 waves
+// owns 128 channels x 128 positions. Each 64-element K chunk of its 128
+// weight rows and 128 patch rows (128 contiguous bytes per row) moves into LDS
+// with global_load_lds, eight whole rows per instruction, double-buffered;
+// the 16-byte chunks of a row are XOR-swizzled by the row so the MFMA
+// fragment reads spread over the banks. Each wave computes 64 x 64 of the
+// tile from LDS.
+constexpr int kBT = 128;   // workgroup tile: channels and positions
+constexpr int kBK = 64;    // K elements per chunk
+
+struct LdsTiles {
+  uint16_t a[2][kBT * kBK];
+  uint16_t b[2][kBT * kBK];
+};
+constexpr int kOutStride = kBT + 4;   // fp32 row of the staged output tile
+constexpr size_t kLdsBytes =
+    sizeof(LdsTiles) > kBT * kOutStride * sizeof(float) ? sizeof(LdsTiles) : kBT * kOutStride * sizeof(float);
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(256) void hr_conv_lds_kernel(ConvArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kLdsBytes];
+  LdsTiles& sm = *reinterpret_cast<LdsTiles*>(lds_raw);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int L = logical_id(blockIdx.x, a.G);
+  const int s = L / (a.m_tiles * a.n_tiles);
+  const int t = L - s * (a.m_tiles * a.n_tiles);
+  const int mt = a.m_slow ? t / a.n_tiles : t % a.m_tiles;
+  const int nt = a.m_slow ? t % a.n_tiles : t / a.m_tiles;
+  const int n0 = nt * kBT;
+  const int m0 = mt * kBT;
+  const int k_begin = __builtin_amdgcn_readfirstlane(s * a.k_chunk);
+  const int k_end = __builtin_amdgcn_readfirstlane(min(a.K, k_begin + a.k_chunk));
+  const int n_chunks = max(0, (k_end - k_begin) / kBK);
+
+  // loader: wave w fills rows 32w .. 32w+31 of both tiles, 8 rows (1 KB) per
+  // instruction; lane L lands on row 32w + 8i + L/8 at physical chunk L%8 and
+  // fetches logical chunk (L%8) ^ (row & 7)
+  const uint16_t* wsrc[4];
+  int64_t xsrc[4];
+  int lchunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * wave + 8 * i + (lane >> 3);
+    lchunk[i] = 8 * ((lane & 7) ^ (row & 7));
+    const int n = min(n0 + row, a.c_out - 1);
+    wsrc[i] = a.w + static_cast<int64_t>(n) * a.K + lchunk[i];
+    const uint32_t m = static_cast<uint32_t>(min(m0 + row, a.M - 1));
+    const uint32_t wo = m % static_cast<uint32_t>(a.Wo);
+    uint32_t r = m / static_cast<uint32_t>(a.Wo);
+    const uint32_t ho = r % static_cast<uint32_t>(a.Ho);
+    r /= static_cast<uint32_t>(a.Ho);
+    const uint32_t to = r % static_cast<uint32_t>(a.To);
+    const uint32_t b = r / static_cast<uint32_t>(a.To);
+    xsrc[i] = (((static_cast<int64_t>(b) * a.T + to * a.kt) * a.H + ho * a.kh) * a.W + wo * a.kw) * a.c_in + lchunk[i];
+  }
+  auto seg_off = [&](int seg) -> int64_t {
+    const int dw = seg % a.kw;
+    const int dh = (seg / a.kw) % a.kh;
+    const int dt = seg / (a.kw * a.kh);
+    return ((static_cast<int64_t>(dt) * a.H + dh) * a.W + dw) * a.c_in;
+  };
+  // chunk cursor (wave-uniform): K element, channel within the segment, segment offset
+  int cur_k = k_begin;
+  int cur_seg = k_begin / a.c_in;
+  int cur_ci = k_begin - cur_seg * a.c_in;
+  int64_t cur_base = seg_off(cur_seg);
+  auto issue = [&](int buf) {
+    const int64_t xoff = cur_base + cur_ci;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row0 = 32 * wave + 8 * i;
+      __builtin_amdgcn_global_load_lds(wsrc[i] + cur_k, (lds_void*)(sm.a[buf] + row0 * kBK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.x + xsrc[i] + xoff, (lds_void*)(sm.b[buf] + row0 * kBK), 16, 0, 0);
+    }
+    cur_k += kBK;
+    cur_ci += kBK;
+    if (cur_ci == a.c_in) {
+      cur_ci = 0;
+      ++cur_seg;
+      cur_base = seg_off(cur_seg);
+    }
+  };
+
+  // compute: wave (wn, wm) = (w & 1, w >> 1) owns channels 64wn.., positions 64wm..
+  const int wn = wave & 1, wm = wave >> 1;
+  int a_off[2][4], b_off[2][4];   // element offsets of the fragments in a tile, per (block, k-step)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ra = 64 * wn + 32 * i + l32;
+      const int rb = 64 * wm + 32 * i + l32;
+      a_off[i][ks] = ra * kBK + 8 * ((2 * ks + g) ^ (ra & 7));
+      b_off[i][ks] = rb * kBK + 8 * ((2 * ks + g) ^ (rb & 7));
+    }
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+
+  if (n_chunks > 0) {
+    issue(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int c = 0; c < n_chunks; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < n_chunks) issue(buf ^ 1);
+      const uint16_t* ta = sm.a[buf];
+      const uint16_t* tb = sm.b[buf];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 af[2], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const bf16x8*>(ta + a_off[i][ks]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(tb + b_off[j][ks]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  }
+
+  // stage the tile in LDS as fp32 [position][channel] (the operand tiles are
+  // no longer read: every wave passed the last barrier), then write whole rows
+  float* tile = reinterpret_cast<float*>(lds_raw);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = 64 * wn + 32 * i + 8 * q + 4 * g;
+        const int pl = 64 * wm + 32 * j + l32;
+        *reinterpret_cast<float4*>(&tile[pl * kOutStride + nl]) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
+  __syncthreads();
+  if (a.n_split == 1) {
+    // 16 threads per position, 8 channels (16 bytes of bf16) each: 16 positions per pass
+#pragma unroll
+    for (int pass = 0; pass < kBT / 16; ++pass) {
+      const int pl = 16 * pass + (tid >> 4);
+      const int nl = 8 * (tid & 15);
+      const int m = m0 + pl;
+      const int n = n0 + nl;
+      if (m >= a.M || n >= a.c_out) continue;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = tile[pl * kOutStride + nl + e] + (a.bias != nullptr ? a.bias[n + e] : 0.f);
+        if (a.act) v[e] = silu(v[e]);
+      }
+      uint4 pk;
+      pk.x = pf::pack_bf16x2(v[0], v[1]);
+      pk.y = pf::pack_bf16x2(v[2], v[3]);
+      pk.z = pf::pack_bf16x2(v[4], v[5]);
+      pk.w = pf::pack_bf16x2(v[6], v[7]);
+      *reinterpret_cast<uint4*>(a.y + static_cast<int64_t>(m) * a.c_out + n) = pk;
+    }
+  } else {
+    // 32 threads per position, 4 channels (16 bytes of fp32) each: 8 positions per pass
+#pragma unroll
+    for (int pass = 0; pass < kBT / 8; ++pass) {
+      const int pl = 8 * pass + (tid >> 5);
+      const int nl = 4 * (tid & 31);
+      const int m = m0 + pl;
+      const int n = n0 + nl;
+      if (m >= a.M || n >= a.c_out) continue;
+      *reinterpret_cast<float4*>(a.part + (static_cast<int64_t>(s) * a.M + m) * a.c_out + n) =
+          *reinterpret_cast<const float4*>(&tile[pl * kOutStride + nl]);
+    }
+  }
+}
+
 // Sum the K-split partials in split order, add the bias, apply SiLU, round.
 __global__ __launch_bounds__(256) void hr_reduce_kernel(ConvArgs a) {
   const int64_t i4 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // 4 channels each
@@ -266,6 +459,7 @@ struct ConvPlan {
   int64_t M = 0;
   int To = 0, Ho = 0, Wo = 0, K = 0;
   int ni = 2, nj = 2;   // wave tile: 32 ni channels x 32 nj positions
+  bool lds = false;     // workgroup-tiled kernel (C_in a multiple of 64)
   int m_tiles = 0, n_tiles = 0, n_split = 1, k_chunk = 0, G = 0;
   size_t ws_bytes = 0;
 };
@@ -286,23 +480,36 @@ ConvPlan make_conv_plan(int n_batch, int T, int H, int W, int c_in, int kt, int 
   p.M = static_cast<int64_t>(n_batch) * p.To * p.Ho * p.Wo;
   p.K = kt * kh * kw * c_in;
   const int64_t target = static_cast<int64_t>(kTargetWaves) * multiprocessors() / 256;
-  // 64 x 64 wave tiles (each fragment feeds two MFMAs) unless the reduction is
-  // only a few steps deep; then the operand reuse is worth less than more waves
-  p.ni = p.nj = (p.K / 16 <= 4) ? 1 : 2;
-  p.m_tiles = static_cast<int>((p.M + 32 * p.nj - 1) / (32 * p.nj));
-  p.n_tiles = (c_out + 32 * p.ni - 1) / (32 * p.ni);
-  const int64_t tiles = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
-  const int steps = p.K / 16;
-  // split K while the grid holds fewer waves than the target, every split
-  // keeps at least 2 * kDepth steps of 16, and the fp32 partials stay under
-  // half the bytes the stage must read anyway (weights + activations)
-  int split = 1;
   const double reads = 2.0 * (static_cast<double>(c_out) * p.K + static_cast<double>(p.M) * p.K);
   const double part_per_split = 4.0 * static_cast<double>(p.M) * c_out;
-  while (split < kMaxSplit && tiles * split * 2 <= target && steps / (split * 2) >= 2 * kDepth &&
-         part_per_split * split * 2 <= 0.5 * reads)
-    split *= 2;
-  p.k_chunk = ((steps + split - 1) / split) * 16;
+  int64_t tiles = 0;
+  int split = 1;
+  p.lds = c_in % kBK == 0;
+  if (p.lds) {
+    // 128 x 128 workgroup tiles (4 waves), K in chunks of 64
+    p.m_tiles = static_cast<int>((p.M + kBT - 1) / kBT);
+    p.n_tiles = (c_out + kBT - 1) / kBT;
+    tiles = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
+    const int chunks = p.K / kBK;
+    while (split < kMaxSplit && 4 * tiles * split * 2 <= target && chunks / (split * 2) >= 4 &&
+           part_per_split * split * 2 <= kPartialBudget * reads)
+      split *= 2;
+    p.k_chunk = ((chunks + split - 1) / split) * kBK;
+  } else {
+    // 64 x 64 wave tiles (each fragment feeds two MFMAs) unless the reduction
+    // is only a few steps deep; then the operand reuse is worth less than more waves
+    p.ni = p.nj = (p.K / 16 <= 4) ? 1 : 2;
+    p.m_tiles = static_cast<int>((p.M + 32 * p.nj - 1) / (32 * p.nj));
+    p.n_tiles = (c_out + 32 * p.ni - 1) / (32 * p.ni);
+    tiles = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
+    const int steps = p.K / 16;
+    // split K while the grid holds fewer waves than the target, every split
+    // keeps at least 2 * kDepth steps of 16 and the partials stay in budget
+    while (split < kMaxSplit && tiles * split * 2 <= target && steps / (split * 2) >= 2 * kDepth &&
+           part_per_split * split * 2 <= kPartialBudget * reads)
+      split *= 2;
+    p.k_chunk = ((steps + split - 1) / split) * 16;
+  }
   p.n_split = (p.K + p.k_chunk - 1) / p.k_chunk;
   p.G = static_cast<int>(tiles * p.n_split);
   p.ws_bytes = p.n_split > 1 ? static_cast<size_t>(p.n_split) * p.M * c_out * sizeof(float) : 0;
@@ -367,7 +574,9 @@ pf_status launch_conv(const pf_bf16* x, int n_batch, int T, int H, int W, int c_
   a.G = p.G;
   // activations (positions x K) against weights (channels x K)
   a.m_slow = p.M > c_out ? 1 : 0;
-  if (p.ni == 2 && p.nj == 2)
+  if (p.lds)
+    hipLaunchKernelGGL(hr_conv_lds_kernel, dim3(p.G), dim3(256), 0, st, a);
+  else if (p.ni == 2 && p.nj == 2)
     hipLaunchKernelGGL((hr_conv_kernel<2, 2>), dim3(p.G), dim3(64), 0, st, a);
   else if (p.ni == 2)
     hipLaunchKernelGGL((hr_conv_kernel<2, 1>), dim3(p.G), dim3(64), 0, st, a);
