@@ -15,6 +15,8 @@ Sources (five web pages on PackForcing, arXiv 2603.25730):
             "Bounded Attention Context", "The Position Misalignment Problem",
             "Incremental RoPE adjustment", "Implementation Details".
   [summary] openbayes English summary, "Method".
+  The HR branch follows [arXiv] "HR Branch: Progressive 3D Convolution" and
+  "Feature Fusion", and [digest] 前置知识 3D卷积.
 
 Readings where the pages are silent (each one is listed with its reason in the
 design notes of the repository):
@@ -32,9 +34,13 @@ design notes of the repository):
   * Attention: one softmax over the concatenation sink || selected mid ||
     recent || current, no mask, scale 1/sqrt(128).
 
+  * HR branch of the compressor: see its section below (kernel = stride, SiLU
+    after each strided stage, a linear projection, bf16 storage per stage).
+
 Parity unpinned (the pages do not fix these, so no test can pin them to the
 pages): whether the scoring rule equals the paper's missing Sec. 3.5 rule, the
-frequency base and pair layout of the paper's backbone, and the placement rule.
+frequency base and pair layout of the paper's backbone, the placement rule, and
+the HR branch's kernel sizes, widths and (trained) weights.
 """
 from __future__ import annotations
 
