@@ -18,8 +18,7 @@ Sources (five web pages on PackForcing, arXiv 2603.25730):
   The HR branch follows [arXiv] "HR Branch: Progressive 3D Convolution" and
   "Feature Fusion", and [digest] 前置知识 3D卷积.
 
-Readings where the pages are silent (each one is listed with its reason in the
-design notes of the repository):
+Readings where the pages are silent:
   * RoPE frequencies: each axis a of width d_a uses theta_{a,j} = base^(-2j/d_a),
     j < d_a/2, base 10000 (RoFormer form); complex pairs are adjacent reals
     (2j, 2j+1); temporal pairs occupy dims 0..43, height 44..85, width 86..127.
@@ -380,7 +379,7 @@ def layer_step(cache: Dict[str, np.ndarray], pos_tags: np.ndarray, n_c: int, top
 # 前置知识 3D卷积 and 方法步骤详情 (2)
 # ---------------------------------------------------------------------------
 #
-# Readings where the pages are silent (listed in the design notes):
+# Readings where the pages are silent:
 #  * each strided convolution has its kernel equal to its stride and no
 #    padding, so every output position sees one disjoint input patch and every
 #    dimension is floored, which is exactly what the N_c formula counts;
