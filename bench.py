@@ -386,34 +386,37 @@ def main():
     def step(i, ev=None):
         fr = (cfg.sink_blocks + M + i) * Bf
         if ev: ev[0].record(stream)
-        pf.pf_score_select(t["q"], t["pool_k"], cfg.n_c, k, ids_out=ids, scores_out=scores, workspace=ws)
+        pf.pf_select_place(t["q"], t["pool_k"], cfg.n_c, k, tags, fr, Bf, ids_out=ids, deltas_out=deltas,
+                           scores_out=scores, workspace=ws)
         if ev: ev[1].record(stream)
-        pf.pf_selection_deltas(ids, tags, fr, Bf, deltas_out=deltas)
-        if ev: ev[2].record(stream)
         pf.pf_rope_shift(t["pool_k"], cfg.n_c, deltas, ids)
-        if ev: ev[3].record(stream)
+        if ev: ev[2].record(stream)
         pf.pf_partition_attn(t["q"], t["sink_k"], t["sink_v"], t["pool_k"], t["pool_v"], cfg.n_c, ids,
                              t["recent_k"], t["recent_v"], t["cur_k"], t["cur_v"], o=o)
-        if ev: ev[4].record(stream)
+        if ev: ev[3].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # the timed steps, with nothing between the launches
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    part = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])   # [steps, 4] ms
-    ms_select, ms_deltas, ms_rope, ms_attn = part.mean(axis=0)
-
+    # the same number of steps again, with an event after each call, for the breakdown
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
+    part = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])   # [steps, 3] ms
+    ms_select, ms_rope, ms_attn = part.mean(axis=0)
     flops = attn_flops(cfg.n, cfg.n_keys, cfg.heads)
     value = flops / (ms_step * 1e-3) / 1e12
     attn_tflops = flops / (ms_attn * 1e-3) / 1e12
@@ -446,11 +449,11 @@ def main():
                      "traffic": traffic_from_counters(),
                      "kernel": "partition_attn_kernel", "flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": attn_bytes},
-        "kernels_ms": {"score_select": round(float(ms_select), 5), "selection_deltas": round(float(ms_deltas), 5),
-                       "rope_shift": round(float(ms_rope), 5), "partition_attn": round(float(ms_attn), 5)},
+        "kernels_ms": {"select_place": round(float(ms_select), 5), "rope_shift": round(float(ms_rope), 5),
+                       "partition_attn": round(float(ms_attn), 5)},
         "attn_tflops": round(attn_tflops, 2),
         "attn_frac_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-        "score_select_gbs": round(sel_bytes / (ms_select * 1e-3) / 1e9, 1),
+        "select_place_gbs": round(sel_bytes / (ms_select * 1e-3) / 1e9, 1),
         "rope_shift_gbs": round(rope_bytes / (ms_rope * 1e-3) / 1e9, 1),
         "input_gen_s": round(t_gen, 2),
     }

@@ -45,6 +45,10 @@ _SIGNATURES = {
     "pf_rope_shift_batched": ([_p, _i64, _i32, _i64, _i64, _p, _p, _i32, _i32, ctypes.c_double, _p], _i32),
     "pf_rollin": ([_p, _p, _p, _i32, _i32, _i32, _p, _p, ctypes.c_int32, _p], _i32),
     "pf_rollin_batched": ([_p, _p, _i64, _p, _i32, _i32, _i32, _i32, _p, _p, _i64, ctypes.c_int32, _i32, _p], _i32),
+    "pf_select_place": ([_p, _i64, _i32, _p, _i32, _i32, _i32, _p, ctypes.c_int32, ctypes.c_int32, _p, _p, _p, _p,
+                         _sz, _p], _i32),
+    "pf_select_place_batched": ([_p, _i64, _i64, _i32, _p, _i64, _i32, _i32, _i32, _p, ctypes.c_int32,
+                                 ctypes.c_int32, _i32, _p, _p, _p, _p, _sz, _p], _i32),
     "pf_hr_conv_workspace_bytes": ([_i32] * 9, _sz),
     "pf_hr_conv": ([_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32, _i32, _p, _p, _sz, _p], _i32),
     "pf_hr_branch_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _p, _i32], _sz),
@@ -142,6 +146,37 @@ def pf_score_select(q, pool_k, n_c: int, top_k: int, ids_out=None, scores_out=No
                                _ptr(scores_out), _ptr(workspace), workspace.numel(), _stream(stream)),
            "pf_score_select")
     return ids_out, scores_out
+
+
+def pf_select_place(q, pool_k, n_c: int, top_k: int, pos_tags, recent_first_frame: int, block_frames: int,
+                    ids_out=None, deltas_out=None, scores_out=None, workspace=None, stream=None):
+    """Selection and placement in one call: the same ids, scores, deltas and tag
+    updates as pf_score_select then pf_selection_deltas. Returns (ids, deltas, scores)."""
+    torch = _torch()
+    heads = int(q.shape[1])
+    n_q = _kv_rows(q, heads, "q")
+    rows = _kv_rows(pool_k, heads, "pool_k")
+    if n_c <= 0 or rows % n_c:
+        raise ValueError("pool rows must be a multiple of n_c")
+    n_blocks = rows // n_c
+    _i32_vec(pos_tags, "pos_tags")
+    if pos_tags is None or pos_tags.numel() != n_blocks:
+        raise ValueError(f"pos_tags must hold {n_blocks} int32 tags")
+    if ids_out is None:
+        ids_out = torch.empty(top_k, dtype=torch.int32, device=q.device)
+    if deltas_out is None:
+        deltas_out = torch.empty(top_k, dtype=torch.int32, device=q.device)
+    if scores_out is None:
+        scores_out = torch.empty(n_blocks, dtype=torch.float32, device=q.device)
+    _i32_vec(ids_out, "ids_out")
+    _i32_vec(deltas_out, "deltas_out")
+    need = pf_score_select_workspace_bytes(n_q, heads, n_blocks, n_c)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.pf_select_place(_ptr(q), n_q, heads, _ptr(pool_k), n_blocks, n_c, top_k, _ptr(pos_tags),
+                               recent_first_frame, block_frames, _ptr(ids_out), _ptr(deltas_out), _ptr(scores_out),
+                               _ptr(workspace), workspace.numel(), _stream(stream)), "pf_select_place")
+    return ids_out, deltas_out, scores_out
 
 
 def pf_score_select_sub(q, pool_k, n_c: int, top_k: int, q_step: int, head_step: int, ids_out=None,
@@ -243,6 +278,40 @@ def pf_score_select_batched(q, pool_k, n_c: int, top_k: int, ids_out=None, score
                                        workspace.numel(), _stream(stream)),
            "pf_score_select_batched")
     return ids_out, scores_out
+
+
+def pf_select_place_batched(q, pool_k, n_c: int, top_k: int, pos_tags, recent_first_frame: int,
+                            block_frames: int, ids_out=None, deltas_out=None, scores_out=None, workspace=None,
+                            stream=None):
+    """pf_select_place over a batch of caches: q [B][n_q][H][128], pool_k [B][M*n_c][H][128],
+    pos_tags int32 [B][M]. Returns (ids [B][top_k], deltas [B][top_k], scores [B][M])."""
+    torch = _torch()
+    nb, n_q, heads, q_stride = _batched_rows(q, "q")
+    nb2, rows, heads2, p_stride = _batched_rows(pool_k, "pool_k")
+    if nb2 != nb or heads2 != heads:
+        raise ValueError("q and pool_k differ in batch or heads")
+    if n_c <= 0 or rows % n_c:
+        raise ValueError("pool rows must be a multiple of n_c")
+    n_blocks = rows // n_c
+    _i32_vec(pos_tags, "pos_tags")
+    if pos_tags is None or pos_tags.numel() != nb * n_blocks:
+        raise ValueError(f"pos_tags must hold {nb} x {n_blocks} int32 tags")
+    if ids_out is None:
+        ids_out = torch.empty((nb, top_k), dtype=torch.int32, device=q.device)
+    if deltas_out is None:
+        deltas_out = torch.empty((nb, top_k), dtype=torch.int32, device=q.device)
+    if scores_out is None:
+        scores_out = torch.empty((nb, n_blocks), dtype=torch.float32, device=q.device)
+    _i32_vec(ids_out, "ids_out")
+    _i32_vec(deltas_out, "deltas_out")
+    need = pf_score_select_batched_workspace_bytes(n_q, heads, n_blocks, n_c, nb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.pf_select_place_batched(_ptr(q), q_stride, n_q, heads, _ptr(pool_k), p_stride, n_blocks, n_c, top_k,
+                                       _ptr(pos_tags), recent_first_frame, block_frames, nb, _ptr(ids_out),
+                                       _ptr(deltas_out), _ptr(scores_out), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)), "pf_select_place_batched")
+    return ids_out, deltas_out, scores_out
 
 
 def pf_selection_deltas_batched(ids, pos_tags, recent_first_frame: int, block_frames: int, deltas_out=None,

@@ -15,8 +15,10 @@
 //   2. qsum:   the Q partials are added per column, 16 interleaved runs of
 //              segments combined in a fixed order;
 //   3. score:  one workgroup per block adds its slices and dots with the Q sum;
-//   4. topk:   one workgroup per cache bitonic-sorts (score desc, index asc)
-//              keys in LDS and writes the first k ids in ascending order.
+//              the last workgroup of a cache to finish (an agent-scope counter
+//              that colsum resets) bitonic-sorts the (score desc, index asc)
+//              keys in LDS, writes the first k ids in ascending order and,
+//              for the fused select-and-place call, places them.
 // Every sum runs in a fixed order that does not depend on the batch, so
 // identical blocks get identical scores, repeated calls give identical bits,
 // and a batched call gives the bits of the single calls.
@@ -44,7 +46,7 @@ struct SelectPlan {
   int ksub;           // slices per pool block
   int sub_rows;       // rows per slice (last slice may be shorter)
   int n_seg;          // segments per cache
-  size_t cache_partials, cache_floats;   // floats per cache: partials, then qsum, then scores
+  size_t cache_partials, cache_floats;   // floats per cache: partials, qsum, scores, finish counter
   size_t bytes;
 };
 
@@ -71,7 +73,7 @@ SelectPlan make_plan(int64_t n_q, int H, int n_blocks, int n_c, int n_batch, int
   p.n_seg = p.nq_seg + n_blocks * p.ksub;
   const size_t cols = static_cast<size_t>(H) * PF_HEAD_DIM;
   p.cache_partials = static_cast<size_t>(p.n_seg) * cols;
-  p.cache_floats = p.cache_partials + cols + static_cast<size_t>(n_blocks);
+  p.cache_floats = p.cache_partials + cols + static_cast<size_t>(n_blocks) + 1;
   p.cache_floats = (p.cache_floats + 63) & ~static_cast<size_t>(63);   // 256-byte aligned per cache
   p.bytes = p.cache_floats * sizeof(float) * static_cast<size_t>(n_batch);
   return p;
@@ -86,12 +88,15 @@ __global__ __launch_bounds__(1024) void colsum_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ pool, int64_t pool_bstride,
                                                       float* __restrict__ ws, int64_t cache_floats, int64_t n_q,
                                                       int nq_seg, int n_c, int ksub, int sub_rows,
-                                                      int64_t row_elems, int q_step, int head_step) {
+                                                      int64_t row_elems, int q_step, int head_step,
+                                                      int64_t counter_off) {
   extern __shared__ float red[];   // [rpar][cw*8]
   const int cw = blockDim.x, rpar = blockDim.y;
   const int x = threadIdx.x, y = threadIdx.y;
   const int seg = blockIdx.x;
   const int64_t b = blockIdx.y;
+  // the score launch that follows counts finished blocks here
+  if (seg == 0 && x == 0 && y == 0) reinterpret_cast<uint32_t*>(ws + b * cache_floats + counter_off)[0] = 0u;
   const uint16_t* base;
   int64_t rows, stride;   // rows of this segment, elements between them
   if (seg < nq_seg) {
@@ -184,17 +189,48 @@ __global__ __launch_bounds__(kQsumCols * kQsumRuns) void qsum_kernel(float* __re
   }
 }
 
+// Ascending order of the key == descending score, then ascending index.
+__device__ __forceinline__ uint64_t rank_key(float s, uint32_t idx) {
+  if (s == 0.f) s = 0.f;   // -0 and +0 tie
+  uint32_t u = __float_as_uint(s);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // ascending float order
+  return (static_cast<uint64_t>(~u) << 32) | idx;
+}
+
+// Placement of the r-th of k selected blocks (ascending ids): it goes to the
+// r-th of k block slots that end right before the recent block; its shift is
+// that slot's first frame minus the frame its keys encode now (the tag).
+__device__ __forceinline__ void place_one(int32_t id, int r, int top_k, int32_t* tags, int n_blocks,
+                                          int32_t recent_first_frame, int32_t block_frames, int32_t* delta) {
+  if (id < 0 || id >= n_blocks) {
+    *delta = 0;
+    return;
+  }
+  const int32_t target = recent_first_frame - (top_k - r) * block_frames;
+  *delta = target - tags[id];
+  tags[id] = target;
+}
+
 // 3. Block score: one workgroup per pool block and cache. Thread t owns the
 // columns t + 256 i; each column's slices are added in slice order, then the
 // products with the Q sum in column order, then a fixed tree over threads.
+// The workgroup that finishes last for its cache then selects (and places).
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(float* __restrict__ ws, int64_t cache_floats,
                                                               int64_t qsum_off, int64_t scores_off,
-                                                              float* __restrict__ scores_out, int n_blocks,
-                                                              int nq_seg, int ksub, int cols, float norm) {
+                                                              int64_t counter_off, float* __restrict__ scores_out,
+                                                              int n_blocks, int nq_seg, int ksub, int cols,
+                                                              float norm, int top_k, int32_t* __restrict__ ids_out,
+                                                              int32_t* __restrict__ tags, int32_t recent_first_frame,
+                                                              int32_t block_frames, int32_t* __restrict__ deltas) {
   __shared__ float red[kScoreThreads];
+  __shared__ uint64_t keys[PF_MAX_BLOCKS];
+  __shared__ uint32_t chosen[PF_MAX_TOPK];
+  __shared__ int32_t sorted_ids[PF_MAX_TOPK];
+  __shared__ int is_last;
   const int blk = blockIdx.x;
   const int t = threadIdx.x;
-  float* cache = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
+  const int64_t b = blockIdx.y;
+  float* cache = ws + b * cache_floats;
   const float* kp = cache + (static_cast<int64_t>(nq_seg) + static_cast<int64_t>(blk) * ksub) * cols;
   float ks[kScoreColsPerThread];
 #pragma unroll
@@ -220,59 +256,57 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(float* __restrict_
     __syncthreads();
   }
   if (t == 0) {
-    const float s = red[0] * norm;
-    cache[scores_off + blk] = s;
-    if (scores_out) scores_out[static_cast<int64_t>(blockIdx.y) * n_blocks + blk] = s;
+    const float sc = red[0] * norm;
+    cache[scores_off + blk] = sc;
+    if (scores_out) scores_out[b * n_blocks + blk] = sc;
+    // release this score, count it; the workgroup that brings the count to
+    // n_blocks sees every score of its cache
+    uint32_t* counter = reinterpret_cast<uint32_t*>(cache + counter_off);
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = prev == static_cast<uint32_t>(n_blocks - 1);
   }
-}
+  __syncthreads();
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-// Ascending order of the key == descending score, then ascending index.
-__device__ __forceinline__ uint64_t rank_key(float s, uint32_t idx) {
-  if (s == 0.f) s = 0.f;   // -0 and +0 tie
-  uint32_t u = __float_as_uint(s);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // ascending float order
-  return (static_cast<uint64_t>(~u) << 32) | idx;
-}
-
-// 4. Top-k: bitonic sort of up to PF_MAX_BLOCKS keys in LDS, one workgroup per cache.
-constexpr int kTopkThreads = 1024;
-
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ ws, int64_t cache_floats,
-                                                             int64_t scores_off, int n_blocks, int top_k,
-                                                             int32_t* __restrict__ ids_out) {
-  __shared__ uint64_t keys[PF_MAX_BLOCKS];
-  __shared__ uint32_t chosen[PF_MAX_TOPK];
-  const float* scores = ws + static_cast<int64_t>(blockIdx.x) * cache_floats + scores_off;
-  int32_t* ids = ids_out + static_cast<int64_t>(blockIdx.x) * top_k;
+  // 4. Top-k: bitonic sort of the (score desc, index asc) keys in LDS.
+  const float* scores = cache + scores_off;
   int P = 1;
   while (P < n_blocks) P <<= 1;
-  for (int i = threadIdx.x; i < P; i += blockDim.x)
+  for (int i = t; i < P; i += kScoreThreads)
     keys[i] = i < n_blocks ? rank_key(scores[i], static_cast<uint32_t>(i)) : ~0ull;
   __syncthreads();
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += blockDim.x) {
+      for (int i = t; i < P; i += kScoreThreads) {
         const int ixj = i ^ j;
         if (ixj > i) {
-          const uint64_t a = keys[i], b = keys[ixj];
+          const uint64_t x0 = keys[i], x1 = keys[ixj];
           const bool up = (i & k) == 0;
-          if ((a > b) == up) {
-            keys[i] = b;
-            keys[ixj] = a;
+          if ((x0 > x1) == up) {
+            keys[i] = x1;
+            keys[ixj] = x0;
           }
         }
       }
       __syncthreads();
     }
   }
-  if (threadIdx.x < top_k) chosen[threadIdx.x] = static_cast<uint32_t>(keys[threadIdx.x] & 0xFFFFFFFFu);
+  // the k winners, written in ascending id order
+  for (int r = t; r < top_k; r += kScoreThreads) chosen[r] = static_cast<uint32_t>(keys[r] & 0xFFFFFFFFu);
   __syncthreads();
-  if (threadIdx.x < top_k) {
-    const uint32_t me = chosen[threadIdx.x];
+  for (int r = t; r < top_k; r += kScoreThreads) {
+    const uint32_t me = chosen[r];
     int rank = 0;
-    for (int r = 0; r < top_k; ++r) rank += chosen[r] < me;
-    ids[rank] = static_cast<int32_t>(me);
+    for (int q = 0; q < top_k; ++q) rank += chosen[q] < me;
+    sorted_ids[rank] = static_cast<int32_t>(me);
+    ids_out[b * top_k + rank] = static_cast<int32_t>(me);
   }
+  if (tags == nullptr) return;
+  __syncthreads();
+  for (int r = t; r < top_k; r += kScoreThreads)
+    place_one(sorted_ids[r], r, top_k, tags + b * n_blocks, n_blocks, recent_first_frame, block_frames,
+              deltas + b * top_k + r);
 }
 
 // Placement, one workgroup per cache.
@@ -283,15 +317,8 @@ __global__ __launch_bounds__(PF_MAX_TOPK) void deltas_kernel(const int32_t* __re
   const int r = threadIdx.x;
   if (r >= top_k) return;
   const int64_t b = blockIdx.x;
-  const int32_t id = ids[b * top_k + r];
-  if (id < 0 || id >= n_blocks) {
-    deltas[b * top_k + r] = 0;
-    return;
-  }
-  const int32_t target = recent_first_frame - (top_k - r) * block_frames;
-  int32_t* t = tags + b * n_blocks + id;
-  deltas[b * top_k + r] = target - *t;
-  *t = target;
+  place_one(ids[b * top_k + r], r, top_k, tags + b * n_blocks, n_blocks, recent_first_frame, block_frames,
+            deltas + b * top_k + r);
 }
 
 bool valid_sizes(int64_t n_q, int n_heads, int n_blocks, int n_c, int n_batch) {
@@ -313,10 +340,13 @@ extern "C" size_t pf_score_select_workspace_bytes(int64_t n_q, int n_heads, int 
 
 namespace {
 
+// tags == nullptr: selection only; otherwise the selected blocks are also
+// placed (tags updated, deltas written) by the workgroup that selects them.
 pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, int n_heads, int q_step,
                        int head_step, const pf_bf16* pool_k, int64_t pool_batch_stride, int n_blocks, int n_c,
                        int top_k, int n_batch, int32_t* ids_out, float* scores_out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, void* stream, int32_t* tags = nullptr,
+                       int32_t recent_first_frame = 0, int32_t block_frames = 1, int32_t* deltas_out = nullptr) {
   PF_REQUIRE_PTR(q);
   PF_REQUIRE_PTR(pool_k);
   PF_REQUIRE_PTR(ids_out);
@@ -361,6 +391,7 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   const int64_t cf = static_cast<int64_t>(p.cache_floats);
   const int64_t qsum_off = static_cast<int64_t>(p.cache_partials);
   const int64_t scores_off = qsum_off + cols;
+  const int64_t counter_off = scores_off + n_blocks;
   const int64_t qs = n_batch > 1 ? q_batch_stride : 0;
   const int64_t ps = n_batch > 1 ? pool_batch_stride : 0;
 
@@ -368,7 +399,7 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   hipLaunchKernelGGL(colsum_kernel, dim3(p.n_seg, n_batch), dim3(p.cw, p.rpar), lds, st,
                      reinterpret_cast<const uint16_t*>(q), qs, reinterpret_cast<const uint16_t*>(pool_k), ps, ws,
                      cf, p.n_q, p.nq_seg, n_c, p.ksub, p.sub_rows, static_cast<int64_t>(n_heads) * PF_HEAD_DIM,
-                     q_step, head_step);
+                     q_step, head_step, counter_off);
   pf_status s = pf::launch_status("pf_score_select (colsum)");
   if (s != PF_OK) return s;
   hipLaunchKernelGGL(qsum_kernel, dim3((cols + kQsumCols - 1) / kQsumCols, n_batch), dim3(kQsumCols * kQsumRuns), 0,
@@ -377,12 +408,9 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   if (s != PF_OK) return s;
   const double norm = 1.0 / (static_cast<double>(p.n_q) * n_c * p.H * sqrt(static_cast<double>(PF_HEAD_DIM)));
   hipLaunchKernelGGL(score_kernel, dim3(n_blocks, n_batch), dim3(kScoreThreads), 0, st, ws, cf, qsum_off,
-                     scores_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols, static_cast<float>(norm));
-  s = pf::launch_status("pf_score_select (score)");
-  if (s != PF_OK) return s;
-  hipLaunchKernelGGL(topk_kernel, dim3(n_batch), dim3(kTopkThreads), 0, st, ws, cf, scores_off, n_blocks, top_k,
-                     ids_out);
-  return pf::launch_status("pf_score_select (topk)");
+                     scores_off, counter_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols,
+                     static_cast<float>(norm), top_k, ids_out, tags, recent_first_frame, block_frames, deltas_out);
+  return pf::launch_status("pf_score_select (score, top-k)");
 }
 
 }  // namespace
@@ -414,6 +442,32 @@ extern "C" pf_status pf_score_select_sub(const pf_bf16* q, int64_t n_q, int n_he
                                          float* scores_out, void* workspace, size_t workspace_bytes, void* stream) {
   return score_select(q, 0, n_q, n_heads, q_step, head_step, pool_k, 0, n_blocks, n_c, top_k, 1, ids_out,
                       scores_out, workspace, workspace_bytes, stream);
+}
+
+extern "C" pf_status pf_select_place_batched(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, int n_heads,
+                                             const pf_bf16* pool_k, int64_t pool_batch_stride, int n_blocks,
+                                             int n_c, int top_k, int32_t* pos_tags, int32_t recent_first_frame,
+                                             int32_t block_frames, int n_batch, int32_t* ids_out,
+                                             int32_t* deltas_out, float* scores_out, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  PF_REQUIRE_PTR(pos_tags);
+  PF_REQUIRE_PTR(deltas_out);
+  PF_REQUIRE(block_frames >= 1, PF_ERR_RANGE, "block_frames must be >= 1");
+  PF_REQUIRE(((reinterpret_cast<uintptr_t>(pos_tags) | reinterpret_cast<uintptr_t>(deltas_out)) & 3u) == 0,
+             PF_ERR_MISALIGNED, "int32 arrays must be 4-byte aligned");
+  return score_select(q, q_batch_stride, n_q, n_heads, 1, 1, pool_k, pool_batch_stride, n_blocks, n_c, top_k,
+                      n_batch, ids_out, scores_out, workspace, workspace_bytes, stream, pos_tags,
+                      recent_first_frame, block_frames, deltas_out);
+}
+
+extern "C" pf_status pf_select_place(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* pool_k,
+                                     int n_blocks, int n_c, int top_k, int32_t* pos_tags,
+                                     int32_t recent_first_frame, int32_t block_frames, int32_t* ids_out,
+                                     int32_t* deltas_out, float* scores_out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return pf_select_place_batched(q, 0, n_q, n_heads, pool_k, 0, n_blocks, n_c, top_k, pos_tags, recent_first_frame,
+                                 block_frames, 1, ids_out, deltas_out, scores_out, workspace, workspace_bytes,
+                                 stream);
 }
 
 extern "C" pf_status pf_selection_deltas_batched(const int32_t* ids, int top_k, int32_t* pos_tags, int n_blocks,

@@ -164,6 +164,31 @@ pf_status pf_selection_deltas_batched(const int32_t* ids, int top_k, int32_t* po
                                       int32_t* deltas_out, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * Selection and placement in one call
+ * [the two passages above: digest 方法步骤详情 (3), arXiv HTML "Compressed Mid
+ *  Tokens"; arXiv HTML "The Position Misalignment Problem", "Incremental RoPE
+ *  adjustment"]
+ *
+ * Same results as pf_score_select followed by pf_selection_deltas with the same
+ * arguments (ids, deltas, updated pos_tags and scores are bit-identical), in
+ * three launches instead of five: the workgroup that scores a cache's last
+ * block also selects and places. Workspace: pf_score_select_workspace_bytes
+ * (batched: pf_score_select_batched_workspace_bytes); concurrent calls must not
+ * share a workspace. Arguments and limits as for the two calls; pos_tags and
+ * deltas_out must not be NULL.
+ * ------------------------------------------------------------------------- */
+pf_status pf_select_place(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* pool_k, int n_blocks,
+                          int n_c, int top_k, int32_t* pos_tags, int32_t recent_first_frame,
+                          int32_t block_frames, int32_t* ids_out, int32_t* deltas_out, float* scores_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+pf_status pf_select_place_batched(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, int n_heads,
+                                  const pf_bf16* pool_k, int64_t pool_batch_stride, int n_blocks, int n_c,
+                                  int top_k, int32_t* pos_tags, int32_t recent_first_frame, int32_t block_frames,
+                                  int n_batch, int32_t* ids_out, int32_t* deltas_out, float* scores_out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * Incremental temporal RoPE shift, in place
  * [PackForcing digest, 前置知识 RoPE (k^(p) = k_raw e^{i theta p}, and
  *  e^{i theta p} e^{i theta delta} = e^{i theta (p+delta)}) and 方法步骤详情 (4);

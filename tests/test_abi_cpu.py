@@ -211,3 +211,15 @@ def test_hr_branch_validation(pf):
     name, msg = _err(pf, call(wsb=need - 1))
     assert name == "PF_ERR_WORKSPACE" and str(need) in msg
     assert _err(pf, call(wsp=None))[0] == "PF_ERR_WORKSPACE"
+
+
+def test_select_place_validation(pf):
+    L = pf.lib
+    need = L.pf_score_select_workspace_bytes(6240, 12, 40, 182)
+    call = lambda **k: L.pf_select_place(A, 6240, 12, B, 40, 182, k.get("top_k", 16), k.get("tags", C), 176, 4,
+                                         A, k.get("deltas", B), None, k.get("ws", C), need, None)
+    assert _err(pf, call(tags=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, call(deltas=None))[0] == "PF_ERR_NULL"
+    assert _err(pf, call(tags=C + 2))[0] == "PF_ERR_MISALIGNED"
+    assert _err(pf, call(top_k=41))[0] == "PF_ERR_RANGE"
+    assert _err(pf, call(ws=None))[0] == "PF_ERR_WORKSPACE"

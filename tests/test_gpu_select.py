@@ -167,3 +167,50 @@ def test_select_subsampled(steps):
     if steps == (1, 1):
         i1, s1 = _select(c, cfg.n_c, cfg.top_k)
         assert ids == i1 and np.array_equal(s.astype(np.float32).view(np.uint32), s1.astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg", [pfgen.C1, pfgen.C2Q, pfgen.C0], ids=lambda c: c.name)
+def test_select_place_fused_equals_separate_calls(cfg):
+    # the fused call gives the bits of pf_score_select + pf_selection_deltas,
+    # over several steps in which the tags keep moving, and the oracle's ids/deltas
+    say(f"test_select_place_fused_equals_separate_calls {cfg.name}")
+    M, k, Bf = cfg.pool_blocks, cfg.top_k, cfg.block_frames
+    fr = (cfg.sink_blocks + M) * Bf
+    tags0 = O.initial_pos_tags(M, cfg.sink_blocks, Bf)
+    t_fused, t_sep, t_ref = dev_i32(tags0), dev_i32(tags0), tags0
+    for step in range(3):
+        c = pfgen.make(cfg, cfg.seed + 40 + step)
+        q, pk = dev(c["q"]), dev(c["pool_k"])
+        ids_f, d_f, s_f = pf.pf_select_place(q, pk, cfg.n_c, k, t_fused, fr, Bf)
+        ids_s, s_s = pf.pf_score_select(q, pk, cfg.n_c, k)
+        d_s = pf.pf_selection_deltas(ids_s, t_sep, fr, Bf)
+        assert ids_f.cpu().numpy().tolist() == ids_s.cpu().numpy().tolist()
+        assert np.array_equal(s_f.cpu().numpy().view(np.uint32), s_s.cpu().numpy().view(np.uint32))
+        assert d_f.cpu().numpy().tolist() == d_s.cpu().numpy().tolist()
+        assert t_fused.cpu().numpy().tolist() == t_sep.cpu().numpy().tolist()
+        ids, flagged = _compare(c, cfg.n_c, k)
+        assert ids == ids_f.cpu().numpy().tolist()
+        d_ref, t_ref = O.placement_deltas(ids, t_ref, fr, Bf)
+        assert d_f.cpu().numpy().tolist() == d_ref.tolist()
+        assert t_fused.cpu().numpy().tolist() == t_ref.tolist()
+
+
+def test_select_place_batched_equals_single_calls():
+    say("test_select_place_batched_equals_single_calls")
+    cfg = pfgen.C2
+    B = 4
+    cs = [pfgen.make(cfg, cfg.seed + 60 + b) for b in range(B)]
+    M, k, Bf = cfg.pool_blocks, cfg.top_k, cfg.block_frames
+    fr = (cfg.sink_blocks + M) * Bf
+    tags0 = O.initial_pos_tags(M, cfg.sink_blocks, Bf)
+    q = dev(np.stack([c["q"] for c in cs]))
+    pk = dev(np.stack([c["pool_k"] for c in cs]))
+    tags = torch.stack([dev_i32(tags0)] * B)
+    ids, d, s = pf.pf_select_place_batched(q, pk, cfg.n_c, k, tags, fr, Bf)
+    for b, c in enumerate(cs):
+        t1 = dev_i32(tags0)
+        i1, d1, s1 = pf.pf_select_place(dev(c["q"]), dev(c["pool_k"]), cfg.n_c, k, t1, fr, Bf)
+        assert ids[b].cpu().numpy().tolist() == i1.cpu().numpy().tolist()
+        assert d[b].cpu().numpy().tolist() == d1.cpu().numpy().tolist()
+        assert np.array_equal(s[b].cpu().numpy().view(np.uint32), s1.cpu().numpy().view(np.uint32))
+        assert tags[b].cpu().numpy().tolist() == t1.cpu().numpy().tolist()
