@@ -35,8 +35,8 @@ PMC_FILE = os.path.join(ROOT, "profiles", "partition_attn_default_hbm_counters.j
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batched selection/RoPE measurement (profiling the layer-step alone)")

@@ -15,8 +15,7 @@
 //   2. qsum:   the Q partials are added per column, 16 interleaved runs of
 //              segments combined in a fixed order;
 //   3. score:  one workgroup per block adds its slices and dots with the Q sum;
-//              the last workgroup of a cache to finish (an agent-scope counter
-//              that colsum resets) bitonic-sorts the (score desc, index asc)
+//   4. topk:   one workgroup per cache bitonic-sorts (score desc, index asc)
 //              keys in LDS, writes the first k ids in ascending order and,
 //              for the fused select-and-place call, places them.
 // Every sum runs in a fixed order that does not depend on the batch, so
@@ -46,7 +45,7 @@ struct SelectPlan {
   int ksub;           // slices per pool block
   int sub_rows;       // rows per slice (last slice may be shorter)
   int n_seg;          // segments per cache
-  size_t cache_partials, cache_floats;   // floats per cache: partials, qsum, scores, finish counter
+  size_t cache_partials, cache_floats;   // floats per cache: partials, then qsum, then scores
   size_t bytes;
 };
 
@@ -73,7 +72,7 @@ SelectPlan make_plan(int64_t n_q, int H, int n_blocks, int n_c, int n_batch, int
   p.n_seg = p.nq_seg + n_blocks * p.ksub;
   const size_t cols = static_cast<size_t>(H) * PF_HEAD_DIM;
   p.cache_partials = static_cast<size_t>(p.n_seg) * cols;
-  p.cache_floats = p.cache_partials + cols + static_cast<size_t>(n_blocks) + 1;
+  p.cache_floats = p.cache_partials + cols + static_cast<size_t>(n_blocks);
   p.cache_floats = (p.cache_floats + 63) & ~static_cast<size_t>(63);   // 256-byte aligned per cache
   p.bytes = p.cache_floats * sizeof(float) * static_cast<size_t>(n_batch);
   return p;
@@ -88,15 +87,12 @@ __global__ __launch_bounds__(1024) void colsum_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ pool, int64_t pool_bstride,
                                                       float* __restrict__ ws, int64_t cache_floats, int64_t n_q,
                                                       int nq_seg, int n_c, int ksub, int sub_rows,
-                                                      int64_t row_elems, int q_step, int head_step,
-                                                      int64_t counter_off) {
+                                                      int64_t row_elems, int q_step, int head_step) {
   extern __shared__ float red[];   // [rpar][cw*8]
   const int cw = blockDim.x, rpar = blockDim.y;
   const int x = threadIdx.x, y = threadIdx.y;
   const int seg = blockIdx.x;
   const int64_t b = blockIdx.y;
-  // the score launch that follows counts finished blocks here
-  if (seg == 0 && x == 0 && y == 0) reinterpret_cast<uint32_t*>(ws + b * cache_floats + counter_off)[0] = 0u;
   const uint16_t* base;
   int64_t rows, stride;   // rows of this segment, elements between them
   if (seg < nq_seg) {
@@ -214,23 +210,14 @@ __device__ __forceinline__ void place_one(int32_t id, int r, int top_k, int32_t*
 // 3. Block score: one workgroup per pool block and cache. Thread t owns the
 // columns t + 256 i; each column's slices are added in slice order, then the
 // products with the Q sum in column order, then a fixed tree over threads.
-// The workgroup that finishes last for its cache then selects (and places).
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(float* __restrict__ ws, int64_t cache_floats,
                                                               int64_t qsum_off, int64_t scores_off,
-                                                              int64_t counter_off, float* __restrict__ scores_out,
-                                                              int n_blocks, int nq_seg, int ksub, int cols,
-                                                              float norm, int top_k, int32_t* __restrict__ ids_out,
-                                                              int32_t* __restrict__ tags, int32_t recent_first_frame,
-                                                              int32_t block_frames, int32_t* __restrict__ deltas) {
+                                                              float* __restrict__ scores_out, int n_blocks,
+                                                              int nq_seg, int ksub, int cols, float norm) {
   __shared__ float red[kScoreThreads];
-  __shared__ uint64_t keys[PF_MAX_BLOCKS];
-  __shared__ uint32_t chosen[PF_MAX_TOPK];
-  __shared__ int32_t sorted_ids[PF_MAX_TOPK];
-  __shared__ int is_last;
   const int blk = blockIdx.x;
   const int t = threadIdx.x;
-  const int64_t b = blockIdx.y;
-  float* cache = ws + b * cache_floats;
+  float* cache = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
   const float* kp = cache + (static_cast<int64_t>(nq_seg) + static_cast<int64_t>(blk) * ksub) * cols;
   float ks[kScoreColsPerThread];
 #pragma unroll
@@ -256,29 +243,35 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(float* __restrict_
     __syncthreads();
   }
   if (t == 0) {
-    const float sc = red[0] * norm;
-    cache[scores_off + blk] = sc;
-    if (scores_out) scores_out[b * n_blocks + blk] = sc;
-    // release this score, count it; the workgroup that brings the count to
-    // n_blocks sees every score of its cache
-    uint32_t* counter = reinterpret_cast<uint32_t*>(cache + counter_off);
-    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = prev == static_cast<uint32_t>(n_blocks - 1);
+    const float s = red[0] * norm;
+    cache[scores_off + blk] = s;
+    if (scores_out) scores_out[static_cast<int64_t>(blockIdx.y) * n_blocks + blk] = s;
   }
-  __syncthreads();
-  if (!is_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
 
-  // 4. Top-k: bitonic sort of the (score desc, index asc) keys in LDS.
-  const float* scores = cache + scores_off;
+// 4. Top-k: bitonic sort of up to PF_MAX_BLOCKS keys in LDS, one workgroup per
+// cache; with tags != nullptr it also places the selected blocks.
+constexpr int kTopkThreads = 1024;
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ ws, int64_t cache_floats,
+                                                             int64_t scores_off, int n_blocks, int top_k,
+                                                             int32_t* __restrict__ ids_out,
+                                                             int32_t* __restrict__ tags, int32_t recent_first_frame,
+                                                             int32_t block_frames, int32_t* __restrict__ deltas) {
+  __shared__ uint64_t keys[PF_MAX_BLOCKS];
+  __shared__ uint32_t chosen[PF_MAX_TOPK];
+  __shared__ int32_t sorted_ids[PF_MAX_TOPK];
+  const int64_t b = blockIdx.x;
+  const float* scores = ws + b * cache_floats + scores_off;
+  int32_t* ids = ids_out + b * top_k;
   int P = 1;
   while (P < n_blocks) P <<= 1;
-  for (int i = t; i < P; i += kScoreThreads)
+  for (int i = threadIdx.x; i < P; i += blockDim.x)
     keys[i] = i < n_blocks ? rank_key(scores[i], static_cast<uint32_t>(i)) : ~0ull;
   __syncthreads();
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = t; i < P; i += kScoreThreads) {
+      for (int i = threadIdx.x; i < P; i += blockDim.x) {
         const int ixj = i ^ j;
         if (ixj > i) {
           const uint64_t x0 = keys[i], x1 = keys[ixj];
@@ -292,21 +285,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(float* __restrict_
       __syncthreads();
     }
   }
-  // the k winners, written in ascending id order
-  for (int r = t; r < top_k; r += kScoreThreads) chosen[r] = static_cast<uint32_t>(keys[r] & 0xFFFFFFFFu);
+  if (threadIdx.x < top_k) chosen[threadIdx.x] = static_cast<uint32_t>(keys[threadIdx.x] & 0xFFFFFFFFu);
   __syncthreads();
-  for (int r = t; r < top_k; r += kScoreThreads) {
-    const uint32_t me = chosen[r];
+  if (threadIdx.x < top_k) {
+    const uint32_t me = chosen[threadIdx.x];
     int rank = 0;
-    for (int q = 0; q < top_k; ++q) rank += chosen[q] < me;
+    for (int r = 0; r < top_k; ++r) rank += chosen[r] < me;
+    ids[rank] = static_cast<int32_t>(me);
     sorted_ids[rank] = static_cast<int32_t>(me);
-    ids_out[b * top_k + rank] = static_cast<int32_t>(me);
   }
   if (tags == nullptr) return;
   __syncthreads();
-  for (int r = t; r < top_k; r += kScoreThreads)
-    place_one(sorted_ids[r], r, top_k, tags + b * n_blocks, n_blocks, recent_first_frame, block_frames,
-              deltas + b * top_k + r);
+  if (threadIdx.x < top_k)
+    place_one(sorted_ids[threadIdx.x], threadIdx.x, top_k, tags + b * n_blocks, n_blocks, recent_first_frame,
+              block_frames, deltas + b * top_k + threadIdx.x);
 }
 
 // Placement, one workgroup per cache.
@@ -391,7 +383,6 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   const int64_t cf = static_cast<int64_t>(p.cache_floats);
   const int64_t qsum_off = static_cast<int64_t>(p.cache_partials);
   const int64_t scores_off = qsum_off + cols;
-  const int64_t counter_off = scores_off + n_blocks;
   const int64_t qs = n_batch > 1 ? q_batch_stride : 0;
   const int64_t ps = n_batch > 1 ? pool_batch_stride : 0;
 
@@ -399,7 +390,7 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   hipLaunchKernelGGL(colsum_kernel, dim3(p.n_seg, n_batch), dim3(p.cw, p.rpar), lds, st,
                      reinterpret_cast<const uint16_t*>(q), qs, reinterpret_cast<const uint16_t*>(pool_k), ps, ws,
                      cf, p.n_q, p.nq_seg, n_c, p.ksub, p.sub_rows, static_cast<int64_t>(n_heads) * PF_HEAD_DIM,
-                     q_step, head_step, counter_off);
+                     q_step, head_step);
   pf_status s = pf::launch_status("pf_score_select (colsum)");
   if (s != PF_OK) return s;
   hipLaunchKernelGGL(qsum_kernel, dim3((cols + kQsumCols - 1) / kQsumCols, n_batch), dim3(kQsumCols * kQsumRuns), 0,
@@ -408,9 +399,12 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   if (s != PF_OK) return s;
   const double norm = 1.0 / (static_cast<double>(p.n_q) * n_c * p.H * sqrt(static_cast<double>(PF_HEAD_DIM)));
   hipLaunchKernelGGL(score_kernel, dim3(n_blocks, n_batch), dim3(kScoreThreads), 0, st, ws, cf, qsum_off,
-                     scores_off, counter_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols,
-                     static_cast<float>(norm), top_k, ids_out, tags, recent_first_frame, block_frames, deltas_out);
-  return pf::launch_status("pf_score_select (score, top-k)");
+                     scores_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols, static_cast<float>(norm));
+  s = pf::launch_status("pf_score_select (score)");
+  if (s != PF_OK) return s;
+  hipLaunchKernelGGL(topk_kernel, dim3(n_batch), dim3(kTopkThreads), 0, st, ws, cf, scores_off, n_blocks, top_k,
+                     ids_out, tags, recent_first_frame, block_frames, deltas_out);
+  return pf::launch_status("pf_score_select (topk)");
 }
 
 }  // namespace
