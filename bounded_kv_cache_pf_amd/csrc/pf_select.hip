@@ -28,7 +28,7 @@
 namespace {
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));   // for the streaming (non-temporal) loads
 
-constexpr int kQSegRows = 128;     // rows of Q per colsum workgroup
+constexpr int kQSegRows = 32;      // rows of Q per colsum workgroup
 constexpr int kTargetSegments = 256;   // pool slices aimed at per cache (at least one per block)
 constexpr int kRowUnroll = 4;      // rows whose loads a colsum thread keeps in flight
 constexpr int kQsumCols = 64;      // columns per qsum workgroup
