@@ -9,11 +9,12 @@
 // the correctly rounded rotation of the stored input.
 //
 // HBM-bound: each row-head reads and writes the 88 bytes of its 44 temporal
-// dims. Eight lanes serve one row-head: lanes 0..5 move 16 bytes each (dims
-// 8c..8c+7), lanes 6 and 7 idle, so a wave touches eight 256-byte row-heads
-// with full-width vector accesses. Lane 5 rotates dims 40..43 and writes dims
-// 44..47 back with their own bits: every store then covers whole 32-byte
-// sectors (bytes 0..95 of the row-head), which avoids partial-sector writes.
+// dims. Eight lanes serve one row-head, 16 bytes each (dims 8c..8c+7), so a
+// wave touches eight 256-byte row-heads with full-width vector accesses. Lanes
+// 0..4 rotate dims 0..39 and lane 5 dims 40..43; lane 5 writes dims 44..47 and
+// lanes 6 and 7 dims 48..63 back with their own bits, so every store covers
+// the row-head's whole first 128-byte line: the caches then never merge a
+// partly written line with the old contents from memory.
 // Each lane's loads are issued before the workgroup computes its fp64 cos/sin
 // table, so the table's latency hides under the memory latency.
 #include <math.h>
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
   for (int pass = 0; pass < kPasses; ++pass) {
     const int64_t rh = rh0 + pass * kRowHeadsPerPass;
     w[pass] = make_uint4(0, 0, 0, 0);
-    if (sub <= 5 && rh < row_heads_per_block) {
+    if (rh < row_heads_per_block) {
       const uint16_t* p = blk_base + rh * PF_HEAD_DIM + sub * 8;
       w[pass] = *reinterpret_cast<const uint4*>(p);
     }
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
     const int64_t rh = rh0 + pass * kRowHeadsPerPass;
-    if (sub > 5 || rh >= row_heads_per_block) break;
+    if (rh >= row_heads_per_block) break;
     uint16_t* p = blk_base + rh * PF_HEAD_DIM + sub * 8;
     if (sub < 5) {
       const int j = sub * 4;
@@ -93,9 +94,11 @@ __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
       rotate_pair(w[pass].z, cs[j + 2], sn[j + 2]);
       rotate_pair(w[pass].w, cs[j + 3], sn[j + 3]);
       *reinterpret_cast<uint4*>(p) = w[pass];
-    } else {
+    } else if (sub == 5) {
       rotate_pair(w[pass].x, cs[20], sn[20]);
       rotate_pair(w[pass].y, cs[21], sn[21]);
+      *reinterpret_cast<uint4*>(p) = w[pass];
+    } else {
       *reinterpret_cast<uint4*>(p) = w[pass];
     }
   }

@@ -196,9 +196,9 @@ pf_status pf_select_place_batched(const pf_bf16* q, int64_t q_batch_stride, int6
  *
  * For every row of each listed block and every head, the 22 temporal complex
  * pairs (dims 2j, 2j+1 for j < 22) are multiplied by e^{+i theta_j delta} with
- * theta_j = rope_base^(-2j/44); dims 44..127 keep their bits (dims 44..47 are
- * stored back unchanged together with dims 40..43, so no other writer may
- * update them concurrently), V is never touched, and a zero delta leaves the
+ * theta_j = rope_base^(-2j/44); dims 44..127 keep their bits (dims 44..63 are
+ * stored back unchanged, so that whole 128-byte lines are written, and no
+ * other writer may update them concurrently), V is never touched, and a zero delta leaves the
  * block's bits unchanged. The angle, its
  * cos/sin and the rotation are fp64; the result is rounded once to bf16
  * (round to nearest even).
