@@ -28,7 +28,10 @@
 namespace {
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));   // for the streaming (non-temporal) loads
 
-constexpr int kQSegRows = 32;      // rows of Q per colsum workgroup
+// rows of Q per colsum workgroup: short, so that one cache's queries spread over
+// as many workgroups as its pool slices; the same for every batch size, so a
+// batched call adds in the order of the single calls
+constexpr int kQSegRows = 32;
 constexpr int kTargetSegments = 256;   // pool slices aimed at per cache (at least one per block)
 constexpr int kRowUnroll = 4;      // rows whose loads a colsum thread keeps in flight
 constexpr int kQsumCols = 64;      // columns per qsum workgroup
