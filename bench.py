@@ -327,6 +327,74 @@ def hr_branch(pf, torch, pfgen, dev, gen_ms, reps=20):
     return out
 
 
+def generation_step(pf, torch, cfg, reps=2):
+    """One full generation step at the 2-minute pool shapes: every layer keeps
+    its own resident cache (sink, a 117-slot pool holding 116 blocks, recent,
+    current) and for each of the denoising steps runs select-and-place, the
+    RoPE shift and the attention; after the steps every layer's new compressed
+    block rolls into slot 116 in one batched call. Queries are drawn once per
+    layer (the kernels do not depend on their values' provenance)."""
+    L, S = cfg.layers, cfg.steps
+    H, n, n_c, M, k, Bf = cfg.heads, cfg.n, cfg.n_c, cfg.pool_blocks, cfg.top_k, cfg.block_frames
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+
+    def draw(rows):
+        return (torch.randn((rows, H, 128), generator=g, device="cuda") * cfg.scale).to(torch.bfloat16)
+
+    layers = []
+    for _ in range(L):
+        c = {"q": draw(n), "sink_k": draw(cfg.n_sink), "sink_v": draw(cfg.n_sink),
+             "pool_k": draw((M + 1) * n_c), "pool_v": draw((M + 1) * n_c), "recent_k": draw(cfg.n_recent),
+             "recent_v": draw(cfg.n_recent), "cur_k": draw(n), "cur_v": draw(n),
+             "tags": ((cfg.sink_blocks + torch.arange(M, device="cuda", dtype=torch.int32)) * Bf).contiguous(),
+             "ids": torch.empty(k, dtype=torch.int32, device="cuda"),
+             "deltas": torch.empty(k, dtype=torch.int32, device="cuda"),
+             "scores": torch.empty(M, dtype=torch.float32, device="cuda")}
+        layers.append(c)
+    blk = torch.stack([draw(n_c) for _ in range(2 * L)]).view(2, L, n_c, H, 128)
+    pool_k_all = [c["pool_k"] for c in layers]
+    ws = torch.empty(pf.pf_score_select_workspace_bytes(n, H, M, n_c), dtype=torch.uint8, device="cuda")
+    o = torch.empty((n, H, 128), dtype=torch.bfloat16, device="cuda")
+    aws = torch.empty(max(pf.pf_partition_attn_workspace_bytes(n, H, cfg.n_keys), 1), dtype=torch.uint8,
+                      device="cuda")
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    fr = (cfg.sink_blocks + M) * Bf
+
+    def one_step():
+        for _ in range(S):
+            for c in layers:
+                pk = c["pool_k"][:M * n_c]
+                pv = c["pool_v"][:M * n_c]
+                pf.pf_select_place(c["q"], pk, n_c, k, c["tags"], fr, Bf, ids_out=c["ids"], deltas_out=c["deltas"],
+                                   scores_out=c["scores"], workspace=ws)
+                pf.pf_rope_shift(pk, n_c, c["deltas"], c["ids"])
+                pf.pf_partition_attn(c["q"], c["sink_k"], c["sink_v"], pk, pv, n_c, c["ids"], c["recent_k"],
+                                     c["recent_v"], c["cur_k"], c["cur_v"], o=o, workspace=aws)
+        # every layer's new compressed block into pool slot M, on a second stream
+        side.wait_stream(main)
+        for li, c in enumerate(layers):
+            pf.pf_rollin(c["pool_k"], c["pool_v"], None, M, blk[0, li], blk[1, li], fr, stream=side)
+        main.wait_stream(side)
+
+    one_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for _ in range(reps):
+        one_step()
+    e1.record(main)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = L * S * attn_flops(n, cfg.n_keys, H)
+    del layers, blk, pool_k_all
+    return {"workload": f"{L} layers x {S} denoising steps at the {M}-block pool shapes ({cfg.n_keys} keys per "
+                        f"layer-step), then {L} roll-ins on a second stream",
+            "ms": round(ms, 3), "layer_steps": L * S, "ms_per_layer_step": round(ms / (L * S), 4),
+            "attention_tflops_over_the_step": round(flops / (ms * 1e-3) / 1e12, 1)}
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -383,6 +451,9 @@ def main():
     o = torch.empty_like(t["q"])
     stream = torch.cuda.current_stream()
 
+    aws = torch.empty(max(pf.pf_partition_attn_workspace_bytes(cfg.n, cfg.heads, cfg.n_keys), 1),
+                      dtype=torch.uint8, device="cuda")
+
     def step(i, ev=None):
         fr = (cfg.sink_blocks + M + i) * Bf
         if ev: ev[0].record(stream)
@@ -392,7 +463,7 @@ def main():
         pf.pf_rope_shift(t["pool_k"], cfg.n_c, deltas, ids)
         if ev: ev[2].record(stream)
         pf.pf_partition_attn(t["q"], t["sink_k"], t["sink_v"], t["pool_k"], t["pool_v"], cfg.n_c, ids,
-                             t["recent_k"], t["recent_v"], t["cur_k"], t["cur_v"], o=o)
+                             t["recent_k"], t["recent_v"], t["cur_k"], t["cur_v"], o=o, workspace=aws)
         if ev: ev[3].record(stream)
 
     for i in range(args.warmup):
@@ -462,6 +533,8 @@ def main():
         t["q"], t["sink_k"], t["sink_v"], t["pool_k"], t["pool_v"], cfg.n_c, ids, t["recent_k"], t["recent_v"],
         t["cur_k"], t["cur_v"], o=o))
     out["hr_branch"] = hr_branch(pf, torch, pfgen, dev, gen_ms=pfgen.C3.layers * pfgen.C3.steps * ms_step)
+    if not args.no_batched:
+        out["generation_step"] = generation_step(pf, torch, pfgen.C3)
     if not args.no_batched:
         hb = hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, 5)
         # one generation step = layers x denoising steps layer-steps; the eviction

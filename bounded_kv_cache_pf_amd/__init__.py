@@ -387,8 +387,12 @@ def pf_rollin_batched(pool_k, pool_v, pos_tags, slot: int, block_k, block_v, fir
            "pf_rollin_batched")
 
 
+def pf_partition_attn_workspace_bytes(n_q: int, n_heads: int, n_keys: int) -> int:
+    return int(lib.pf_partition_attn_workspace_bytes(n_q, n_heads, n_keys))
+
+
 def pf_partition_attn(q, sink_k, sink_v, pool_k, pool_v, n_c: int, mid_ids, recent_k, recent_v, cur_k, cur_v,
-                      scale: float = 0.0, o=None, lse=None, want_lse: bool = False, stream=None):
+                      scale: float = 0.0, o=None, lse=None, want_lse: bool = False, workspace=None, stream=None):
     """softmax(scale Q K^T) V over sink || pool[mid_ids] || recent || cur. Returns (o, lse or None)."""
     torch = _torch()
     heads = int(q.shape[1])
@@ -415,14 +419,18 @@ def pf_partition_attn(q, sink_k, sink_v, pool_k, pool_v, n_c: int, mid_ids, rece
     if lse is None and want_lse:
         lse = torch.empty((heads, n_q), dtype=torch.float32, device=q.device)
     need = int(lib.pf_partition_attn_workspace_bytes(n_q, heads, n_sink + n_sel * n_c + n_rec + n_cur))
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    if workspace is not None:
+        ws, have = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+        have = need
     _check(lib.pf_partition_attn(_ptr(q), n_q, heads,
                                  _ptr(sink_k), _ptr(sink_v), n_sink,
                                  _ptr(pool_k) if n_sel else None, _ptr(pool_v) if n_sel else None, n_blocks,
                                  n_c, _ptr(mid_ids) if n_sel else None, n_sel,
                                  _ptr(recent_k), _ptr(recent_v), n_rec,
                                  _ptr(cur_k), _ptr(cur_v), n_cur,
-                                 float(scale), _ptr(o), _ptr(lse), _ptr(ws), need, _stream(stream)),
+                                 float(scale), _ptr(o), _ptr(lse), _ptr(ws), have, _stream(stream)),
            "pf_partition_attn")
     return o, lse
 
