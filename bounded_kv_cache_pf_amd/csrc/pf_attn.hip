@@ -24,9 +24,14 @@
 //    half of one query's 128 scores and the other half-wave the rest: the row
 //    max needs one swap between half-waves, the row sum none, and the probabilities are already in the B-operand layout of
 //    O^T = V^T P^T. V is read with the gfx950 transposing LDS read.
-//  * Online softmax in the log2 domain. The running max is only raised when a
-//    tile's max exceeds it by more than 2^8, so the O rescale (a wave-uniform
-//    branch) runs on a handful of tiles; exp2 arguments stay <= 8 in between.
+//  * Online softmax in the log2 domain, with a fast path: a tile's scores are
+//    exponentiated against the running max without searching for the tile's
+//    own max. Only a row's first tile, a tile with masked keys, or a tile whose
+//    row sum passes 2^64 (a score far above the running max) takes the exact
+//    path: its scores are recomputed from LDS, the max is searched, and the
+//    running max is raised when the tile's max exceeds it by more than 2^8
+//    (then O is rescaled; a wave-uniform branch). Probabilities and O stay
+//    far inside the fp32 and bf16 range either way.
 //  * Scheduling: with G resident workgroups and U units, the first
 //    floor(U/G) rounds give every workgroup whole units, numbered so that each
 //    XCD walks consecutive units of one head in lockstep (shared K/V in its
@@ -58,6 +63,7 @@ constexpr int kLoadsPerWave = kRowsPerWave / 4;   // four rows (1 KB) per load i
 constexpr int kOcc = 1;                  // workgroups per CU the kernel is built for
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.0f;    // log2 units: p may grow to 2^8 before a rescale
+constexpr float kPsumLimit = 0x1p64f;     // fast-path row sums above this take the exact path
 constexpr int kMinTailTiles = 16;        // shortest run of key tiles worth a partial
 constexpr size_t kPartFloats = static_cast<size_t>(kBM) * D + 2 * kBM;   // U, m, l
 constexpr size_t kPartBytes = kPartFloats * 4;
@@ -293,7 +299,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
     // operand i: dims 16st.. (st = i/kNB) of key block kb = i%kNB, so the kNB
     // accumulator chains alternate; operand i+kRing-1 is read while MFMA i issues
     floatx16 s[kNB];
-    {
+    auto qk = [&]() {
       auto load_k = [&](int i) { return *reinterpret_cast<const bf16x8*>(kt_lds + (i % kNB) * 32 * D + k_off[i / kNB]); };
       bf16x8 op[kRing];
 #pragma unroll
@@ -305,50 +311,69 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
                                                            0, 0, 0);
       }
       sched_ring<8 * kNB, 1>();
-    }
+    };
+    qk();
 
-    // ---- mask keys that do not exist ----
+    // ---- online softmax (log2 domain, lazy rescale) ----
+    // Fast path: exponentiate against the running max without looking for the
+    // tile's max; the tile only needs the exact path (mask, max, rescale) when
+    // it has masked keys, is a row's first tile, or a probability grew past
+    // 2^64 (seen in the row sum), and then its scores are recomputed from LDS.
     const bool need_mask = (k0 + kBN > a.e_cur) || (bad_ids && k0 < a.e_mid && k0 + kBN > a.e_sink);
-    if (need_mask) {
+    bool slow = need_mask || __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+    float psum = 0.f;
+    if (!slow) {
 #pragma unroll
       for (int kb = 0; kb < kNB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (sm.kbad[buf][key]) s[kb][i] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_run));
+          s[kb][i] = p;
+          psum += p;
+        }
+      slow = __builtin_amdgcn_ballot_w64(!(psum <= kPsumLimit)) != 0;
+      if (slow) qk();
+    }
+    if (slow) {
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < kNB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (sm.kbad[buf][key]) s[kb][i] = -INFINITY;
+          }
+      }
+      float mx = s[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+      for (int kb = 1; kb < kNB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = half_swap_max(mx) * a.scale_log2;
+      const bool grow = mx > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < kNB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_use));
+          s[kb][i] = p;
+          psum += p;
         }
     }
-
-    // ---- online softmax (log2 domain, lazy rescale) ----
-    float mx = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-    for (int kb = 1; kb < kNB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = half_swap_max(mx) * a.scale_log2;
-    const bool grow = mx > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < kNB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_use));
-        s[kb][i] = p;
-        psum += p;
-      }
     l_run += psum;
 
     // ---- P^T as the B operand: chunk c covers keys 16c .. 16c+15 ----

@@ -180,3 +180,24 @@ def test_attn_whole_rounds_and_tail_only_plans():
                  pool_k=_bits(rng, 4 * 9, H, 0.7), pool_v=_bits(rng, 4 * 9, H, 0.7), recent_k=_bits(rng, 64, H, 0.7),
                  recent_v=_bits(rng, 64, H, 0.7), cur_k=_bits(rng, 100, H, 0.7), cur_v=_bits(rng, 100, H, 0.7))
         _compare(c, 9, [3, 0], rows=_sample_rows(n_q, H, extra=16), label=f"H={H} n_q={n_q}")
+
+
+@pytest.mark.parametrize("boost", [20.0, 70.0])
+def test_attn_late_dominant_keys(boost):
+    # a few keys near the end of the context score `boost` nats above the rest:
+    # the running max must move up by far more than the lazy-rescale slack
+    # (70 nats = 101 in log2 units) after many tiles have been accumulated
+    say(f"test_attn_late_dominant_keys boost {boost}")
+    rng = np.random.default_rng(int(boost))
+    H, n_q = 2, 300
+    u = rng.standard_normal((H, 128))
+    q = O.f64_to_bf16(u[None] + 0.1 * rng.standard_normal((n_q, H, 128)))
+    qf = O.bf16_to_f64(q).mean(axis=0)                      # [H][128]
+    cur = 0.3 * rng.standard_normal((400, H, 128))
+    for key in (390, 391, 396):
+        cur[key] = qf * (boost * np.sqrt(128.0) / np.sum(qf * qf, axis=1))[:, None]
+    c = dict(q=q, sink_k=_bits(rng, 1000, H, 0.3), sink_v=_bits(rng, 1000, H),
+             pool_k=_bits(rng, 4 * 20, H, 0.3), pool_v=_bits(rng, 4 * 20, H),
+             recent_k=_bits(rng, 500, H, 0.3), recent_v=_bits(rng, 500, H),
+             cur_k=O.f64_to_bf16(cur), cur_v=_bits(rng, 400, H))
+    _compare(c, 20, [1, 3], label=f"late keys +{boost} nats")
