@@ -37,6 +37,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "pf_internal.h"
 
@@ -464,12 +465,19 @@ struct ConvPlan {
   size_t ws_bytes = 0;
 };
 
+// CUs of the current device, looked up once per device
 int multiprocessors() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  return cus;
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
 }
 
 ConvPlan make_conv_plan(int n_batch, int T, int H, int W, int c_in, int kt, int kh, int kw, int c_out) {
