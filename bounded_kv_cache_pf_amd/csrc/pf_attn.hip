@@ -22,8 +22,9 @@
 //    at the end resolve each row.
 //  * The score tile is computed transposed, S^T = K Q^T, so each lane holds
 //    half of one query's 128 scores and the other half-wave the rest: the row
-//    max needs one swap between half-waves, the row sum none, and the probabilities are already in the B-operand layout of
-//    O^T = V^T P^T. V is read with the gfx950 transposing LDS read.
+//    max needs one swap between half-waves, the row sum none, and the
+//    probabilities are already in the B-operand layout of O^T = V^T P^T. V is
+//    read with the gfx950 transposing LDS read.
 //  * Online softmax in the log2 domain, with a fast path: a tile's scores are
 //    exponentiated against the running max without searching for the tile's
 //    own max. Only a row's first tile, a tile with masked keys, or a tile whose
