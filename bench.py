@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -54,11 +55,14 @@ def attn_flops(n_q, n_k, heads):
     return 4.0 * n_q * n_k * 128 * heads
 
 
-def kernel_source_sha():
-    h = hashlib.sha256()
-    with open(os.path.join(ROOT, "bounded_kv_cache_pf_amd", "csrc", "pf_attn.hip"), "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+def kernel_source_sha(text=None):
+    """Hash of the attention kernel's source with comments and blank space
+    removed, so that only a change to the code voids the stored counters."""
+    if text is None:
+        with open(os.path.join(ROOT, "bounded_kv_cache_pf_amd", "csrc", "pf_attn.hip")) as f:
+            text = f.read()
+    code = [re.sub(r"//.*$", "", line).strip() for line in text.splitlines()]
+    return hashlib.sha256("\n".join(c for c in code if c).encode()).hexdigest()[:16]
 
 
 def traffic_from_counters():
