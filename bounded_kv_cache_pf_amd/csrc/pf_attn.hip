@@ -102,33 +102,6 @@ struct AttnArgs {
   float scale_log2;
 };
 
-__device__ __forceinline__ bool resolve_key(const AttnArgs& a, const int32_t* ids_lds, int32_t kk,
-                                            const uint16_t*& kp, const uint16_t*& vp) {
-  int64_t row;
-  if (kk < a.e_sink) {
-    kp = a.k_sink; vp = a.v_sink; row = kk;
-  } else if (kk < a.e_mid) {
-    const int32_t x = kk - a.e_sink;
-    const int32_t b = x / a.n_c;
-    const int32_t id = ids_lds[b];
-    if (id < 0 || id >= a.n_blocks) {
-      kp = a.k_safe; vp = a.v_safe;
-      return false;
-    }
-    kp = a.k_pool; vp = a.v_pool; row = static_cast<int64_t>(id) * a.n_c + (x - b * a.n_c);
-  } else if (kk < a.e_rec) {
-    kp = a.k_rec; vp = a.v_rec; row = kk - a.e_mid;
-  } else if (kk < a.e_cur) {
-    kp = a.k_cur; vp = a.v_cur; row = kk - a.e_rec;
-  } else {
-    kp = a.k_safe; vp = a.v_safe;
-    return false;
-  }
-  kp += row * a.row_stride;
-  vp += row * a.row_stride;
-  return true;
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // LDS row r stores its 16-byte chunk j at position j ^ swz(r). swz is a
@@ -137,50 +110,165 @@ typedef __attribute__((address_space(3))) void lds_void;
 // transposing V read lands on 16 distinct chunks as well.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// Issue the loads of key tile kt (keys kt*kBN ..) into LDS buffers ks/vs.
-// Wave w fills rows 16w .. 16w+15, four rows (1 KB) per instruction; lane L
-// lands on row 16w + 4i + L/16 at physical chunk L%16, so it fetches logical
-// chunk (L%16) ^ swz(row). lane_off[i] holds that lane's element offset within
-// a contiguous partition: (L/16) rows plus the logical chunk.
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, const int32_t* ids_lds, int h, int32_t kt,
-                                           uint16_t* ks, uint16_t* vs, uint8_t* kbad, int wave_u, int lane,
-                                           const int* lane_off) {
+// Tiles are loaded with raw buffer loads straight into LDS (16 bytes per
+// lane, no register staging). Word 3 of a gfx9-family buffer descriptor:
+// 32-bit data format, everything else zero. Offsets are 32-bit, so each
+// descriptor starts near the rows it serves (a tile's first row in its
+// partition; the pool, whose rows the ids scatter, from its start).
+constexpr int kRsrcWord3 = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const uint16_t* p, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, static_cast<int>(n), kRsrcWord3);
+}
+
+// One 1 KB load: 64 lanes x 16 bytes from descriptor r at byte offset voff
+// into four consecutive 256-byte LDS rows starting at lds.
+__device__ __forceinline__ void dma16(rsrc_t r, uint16_t* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Tile layout in LDS: wave w fills rows kRowsPerWave*w .., four rows (1 KB)
+// per load; lane L lands on row kRowsPerWave*w + 4i + L/16 at physical chunk
+// L%16, so it fetches logical chunk (L%16) ^ swz(row).
+__device__ __forceinline__ int tile_row(int wave_u, int lane, int i) {
+  return kRowsPerWave * wave_u + 4 * i + (lane >> 4);
+}
+__device__ __forceinline__ int chunk_bytes(int lane, int row) { return ((lane & 15) ^ swz(row)) << 4; }
+
+// A tile whose loads can be spread over the MFMAs: one descriptor pair and
+// this lane's byte offset for each of the wave's loads.
+struct TileSrc {
+  rsrc_t k, v;
+  int voff[kLoadsPerWave];
+};
+
+// Tile inside one contiguous partition (sink, recent or current).
+__device__ __forceinline__ bool contiguous_tile(const AttnArgs& a, int h, int32_t kt, int wave_u, int lane,
+                                                TileSrc& t) {
   const int32_t k0 = kt * kBN;
-  // fast path: the whole tile lies inside one contiguous partition (uniform)
-  const uint16_t* kbase = nullptr;
-  const uint16_t* vbase = nullptr;
-  int32_t r0 = 0;
+  const uint16_t* kb;
+  const uint16_t* vb;
+  int32_t r0, rows;
   if (k0 + kBN <= a.e_sink) {
-    kbase = a.k_sink; vbase = a.v_sink; r0 = k0;
+    kb = a.k_sink; vb = a.v_sink; r0 = k0; rows = a.e_sink;
   } else if (k0 >= a.e_mid && k0 + kBN <= a.e_rec) {
-    kbase = a.k_rec; vbase = a.v_rec; r0 = k0 - a.e_mid;
+    kb = a.k_rec; vb = a.v_rec; r0 = k0 - a.e_mid; rows = a.e_rec - a.e_mid;
   } else if (k0 >= a.e_rec && k0 + kBN <= a.e_cur) {
-    kbase = a.k_cur; vbase = a.v_cur; r0 = k0 - a.e_rec;
+    kb = a.k_cur; vb = a.v_cur; r0 = k0 - a.e_rec; rows = a.e_cur - a.e_rec;
+  } else {
+    return false;
   }
-  if (kbase != nullptr) {
-    const int64_t off0 = (static_cast<int64_t>(r0) + kRowsPerWave * wave_u) * a.row_stride + h * D;
-#pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-      const int64_t off = off0 + 4 * i * a.row_stride;
-      const int lds_row = kRowsPerWave * wave_u + 4 * i;
-      __builtin_amdgcn_global_load_lds(kbase + off + lane_off[i], (lds_void*)(ks + lds_row * D), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + off + lane_off[i], (lds_void*)(vs + lds_row * D), 16, 0, 0);
-    }
-    return;
-  }
-  // general path: resolve each row (mid blocks through the ids, masked rows)
-  const int pchunk = lane & 15;
+  const int64_t off = static_cast<int64_t>(r0) * a.row_stride + h * D;
+  const int64_t bytes = (static_cast<int64_t>(rows - r0) * a.row_stride - h * D) * 2;
+  t.k = make_rsrc(kb + off, bytes);
+  t.v = make_rsrc(vb + off, bytes);
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
-    const int row = kRowsPerWave * wave_u + 4 * i + (lane >> 4);
-    const uint16_t* kp;
-    const uint16_t* vp;
-    const bool ok = resolve_key(a, ids_lds, k0 + row, kp, vp);
-    const int off = h * D + ((pchunk ^ swz(row)) << 3);
-    const int lds_row = kRowsPerWave * wave_u + 4 * i;
-    __builtin_amdgcn_global_load_lds(kp + off, (lds_void*)(ks + lds_row * D), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vp + off, (lds_void*)(vs + lds_row * D), 16, 0, 0);
-    if (pchunk == 0) kbad[row] = ok ? 0 : 1;
+    const int row = tile_row(wave_u, lane, i);
+    t.voff[i] = static_cast<int>(row * a.row_stride * 2) + chunk_bytes(lane, row);
+  }
+  return true;
+}
+
+// Tile of mid keys only: rows of the selected pool blocks, found through the
+// ids. Rows of an invalid id read pool row 0 and are flagged in kbad.
+__device__ __forceinline__ bool mid_tile(const AttnArgs& a, const int32_t* ids_lds, int h, int32_t kt, int wave_u,
+                                         int lane, uint8_t* kbad, TileSrc& t) {
+  const int32_t k0 = kt * kBN;
+  if (k0 < a.e_sink || k0 + kBN > a.e_mid) return false;
+  const int64_t hb = static_cast<int64_t>(h) * D;
+  const int64_t bytes = (static_cast<int64_t>(a.n_blocks) * a.n_c * a.row_stride - hb) * 2;
+  t.k = make_rsrc(a.k_pool + hb, bytes);
+  t.v = make_rsrc(a.v_pool + hb, bytes);
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int row = tile_row(wave_u, lane, i);
+    const int32_t x = k0 + row - a.e_sink;
+    const int32_t b = x / a.n_c;
+    const int32_t id = ids_lds[b];
+    const bool ok = id >= 0 && id < a.n_blocks;
+    const int64_t prow = ok ? static_cast<int64_t>(id) * a.n_c + (x - b * a.n_c) : 0;
+    t.voff[i] = static_cast<int>(prow * a.row_stride * 2) + chunk_bytes(lane, row);
+    if ((lane & 15) == 0) kbad[row] = ok ? 0 : 1;
+  }
+  return true;
+}
+
+// Load j (0 .. 2*kLoadsPerWave-1: the K loads, then the V loads) of this
+// wave's share of a spreadable tile.
+__device__ __forceinline__ void load_part(const TileSrc& t, int j, uint16_t* ks, uint16_t* vs, int wave_u) {
+  const int i = j % kLoadsPerWave;
+  const int lds_row = kRowsPerWave * wave_u + 4 * i;
+  if (j < kLoadsPerWave)
+    dma16(t.k, ks + lds_row * D, t.voff[i]);
+  else
+    dma16(t.v, vs + lds_row * D, t.voff[i]);
+}
+
+// Any tile, row by row: each lane resolves its key to a partition and a row
+// there (mid keys through the ids; keys past the end and rows of an invalid id
+// read the safe row and are flagged in kbad). One load per partition present
+// among a load's lanes, masked to those lanes. Used for the tiles that
+// straddle a partition boundary or run past the last key.
+__device__ __forceinline__ void load_general(const AttnArgs& a, const int32_t* ids_lds, int h, int32_t kt,
+                                             uint16_t* ks, uint16_t* vs, uint8_t* kbad, int wave_u, int lane) {
+  const int32_t k0 = kt * kBN;
+  const int64_t hb = static_cast<int64_t>(h) * D;
+  const int64_t rs = a.row_stride;
+  // first row of each contiguous partition the descriptors start at
+  const int32_t b_sink = k0;
+  const int32_t b_rec = (k0 > a.e_mid ? k0 : a.e_mid) - a.e_mid;
+  const int32_t b_cur = (k0 > a.e_rec ? k0 : a.e_rec) - a.e_rec;
+  int part[kLoadsPerWave], voff[kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int row = tile_row(wave_u, lane, i);
+    const int32_t kk = k0 + row;
+    int pt = 4;
+    int64_t prow = 0;
+    if (kk < a.e_sink) {
+      pt = 0; prow = kk - b_sink;
+    } else if (kk < a.e_mid) {
+      const int32_t x = kk - a.e_sink;
+      const int32_t b = x / a.n_c;
+      const int32_t id = ids_lds[b];
+      if (id >= 0 && id < a.n_blocks) {
+        pt = 1; prow = static_cast<int64_t>(id) * a.n_c + (x - b * a.n_c);
+      }
+    } else if (kk < a.e_rec) {
+      pt = 2; prow = kk - a.e_mid - b_rec;
+    } else if (kk < a.e_cur) {
+      pt = 3; prow = kk - a.e_rec - b_cur;
+    }
+    part[i] = pt;
+    voff[i] = static_cast<int>(prow * rs * 2) + chunk_bytes(lane, row);
+    if ((lane & 15) == 0) kbad[row] = pt == 4 ? 1 : 0;
+  }
+#pragma unroll
+  for (int pt = 0; pt < 5; ++pt) {
+    const uint16_t* kb = pt == 0 ? a.k_sink : pt == 1 ? a.k_pool : pt == 2 ? a.k_rec : pt == 3 ? a.k_cur : a.k_safe;
+    const uint16_t* vb = pt == 0 ? a.v_sink : pt == 1 ? a.v_pool : pt == 2 ? a.v_rec : pt == 3 ? a.v_cur : a.v_safe;
+    const int64_t first = pt == 0 ? b_sink : pt == 2 ? b_rec : pt == 3 ? b_cur : 0;
+    const int64_t rows = pt == 0   ? a.e_sink
+                         : pt == 1 ? static_cast<int64_t>(a.n_blocks) * a.n_c
+                         : pt == 2 ? a.e_rec - a.e_mid
+                         : pt == 3 ? a.e_cur - a.e_rec
+                                   : 1;
+    const int64_t off = first * rs + hb;
+    const int64_t bytes = ((rows - first) * rs - hb) * 2;
+    const rsrc_t rk = make_rsrc(kb + off, bytes);
+    const rsrc_t rv = make_rsrc(vb + off, bytes);
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      if (__builtin_amdgcn_ballot_w64(part[i] == pt) == 0) continue;
+      if (part[i] == pt) {
+        const int lds_row = kRowsPerWave * wave_u + 4 * i;
+        dma16(rk, ks + lds_row * D, voff[i]);
+        dma16(rv, vs + lds_row * D, voff[i]);
+      }
+    }
   }
 }
 
@@ -203,19 +291,21 @@ __device__ __forceinline__ short4v lds_read_tr(const uint16_t* p) {
 // reads of operand i+kRing-1, in that order in the final schedule.
 constexpr int kRing = 3;
 
-template <int N, int RPO, int I>
+// With DM > 0, a vector-memory load follows every DM-th MFMA as well.
+template <int N, int RPO, int DM, int I>
 __device__ __forceinline__ void sched_ring_step() {
   if constexpr (I < N) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if constexpr (I + kRing - 1 < N) __builtin_amdgcn_sched_group_barrier(0x100, RPO, 0);
-    sched_ring_step<N, RPO, I + 1>();
+    if constexpr (DM > 0 && I % DM == DM - 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    sched_ring_step<N, RPO, DM, I + 1>();
   }
 }
 
-template <int N, int RPO>
+template <int N, int RPO, int DM = 0>
 __device__ __forceinline__ void sched_ring() {
   __builtin_amdgcn_sched_group_barrier(0x100, (kRing - 1) * RPO, 0);
-  sched_ring_step<N, RPO, 0>();
+  sched_ring_step<N, RPO, DM, 0>();
 }
 
 struct Smem {
@@ -274,27 +364,36 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
     v_lo[db] = v_r * D + (((4 * db + v_x) ^ swz(v_r)) << 3) + v_h;
     v_hi[db] = (v_r + 8) * D + (((4 * db + v_x) ^ swz(v_r + 8)) << 3) + v_h;
   }
-  // tile loader: element offset of this lane inside a contiguous partition
-  int lane_off[kLoadsPerWave];
+  {
+    TileSrc t;
+    if (contiguous_tile(a, h, kt0, wave_u, lane, t) || mid_tile(a, sm.ids, h, kt0, wave_u, lane, sm.kbad[0], t)) {
 #pragma unroll
-  for (int i = 0; i < kLoadsPerWave; ++i)
-    lane_off[i] = static_cast<int>((lane >> 4) * a.row_stride) +
-                  (((lane & 15) ^ swz(kRowsPerWave * wave + 4 * i + (lane >> 4))) << 3);
-
-  issue_tile(a, sm.ids, h, kt0, sm.ks[0], sm.vs[0], sm.kbad[0], wave_u, lane, lane_off);
+      for (int j = 0; j < 2 * kLoadsPerWave; ++j) load_part(t, j, sm.ks[0], sm.vs[0], wave_u);
+    } else {
+      load_general(a, sm.ids, h, kt0, sm.ks[0], sm.vs[0], sm.kbad[0], wave_u, lane);
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   const bool bad_ids = sm.any_bad_id != 0;
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
+  // One key tile. The tile's buffers and the next tile's are distinct, and
+  // saying so (restrict) lets the compiler see that the LDS reads of this
+  // tile do not wait for the loads of the next one in flight.
+  auto step = [&](int32_t kt, const uint16_t* __restrict__ kt_lds, const uint16_t* __restrict__ vt_lds,
+                  const uint8_t* __restrict__ kbad_cur, uint16_t* __restrict__ k_next,
+                  uint16_t* __restrict__ v_next, uint8_t* __restrict__ kbad_next) {
     const int32_t k0 = kt * kBN;
-    if (kt + 1 < kt1)
-      issue_tile(a, sm.ids, h, kt + 1, sm.ks[buf ^ 1], sm.vs[buf ^ 1], sm.kbad[buf ^ 1], wave_u, lane,
-                 lane_off);
-
-    const uint16_t* kt_lds = sm.ks[buf];
-    const uint16_t* vt_lds = sm.vs[buf];
+    // Next tile: inside one partition its loads are spread over the QK MFMAs
+    // below (in a burst they would stall the issuing waves behind the
+    // vector-memory address queue); a tile across a boundary loads here.
+    TileSrc nt;
+    bool spread = false;
+    if (kt + 1 < kt1) {
+      spread = contiguous_tile(a, h, kt + 1, wave_u, lane, nt) ||
+               mid_tile(a, sm.ids, h, kt + 1, wave_u, lane, kbad_next, nt);
+      if (!spread) load_general(a, sm.ids, h, kt + 1, k_next, v_next, kbad_next, wave_u, lane);
+    }
 
     // ---- S^T = K Q^T for kNB 32-key blocks ----
     // operand i: dims 16st.. (st = i/kNB) of key block kb = i%kNB, so the kNB
@@ -313,7 +412,24 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
       }
       sched_ring<8 * kNB, 1>();
     };
-    qk();
+    if (spread) {
+      // the same products with the next tile's loads, one per kDm MFMAs
+      constexpr int kDm = 8 * kNB / (2 * kLoadsPerWave);
+      auto load_k = [&](int i) { return *reinterpret_cast<const bf16x8*>(kt_lds + (i % kNB) * 32 * D + k_off[i / kNB]); };
+      bf16x8 op[kRing];
+#pragma unroll
+      for (int r = 0; r < kRing - 1; ++r) op[r] = load_k(r);
+#pragma unroll
+      for (int i = 0; i < 8 * kNB; ++i) {
+        if (i + kRing - 1 < 8 * kNB) op[(i + kRing - 1) % kRing] = load_k(i + kRing - 1);
+        s[i % kNB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % kRing], qf[i / kNB], i < kNB ? floatx16{} : s[i % kNB],
+                                                           0, 0, 0);
+        if (i % kDm == kDm - 1) load_part(nt, i / kDm, k_next, v_next, wave_u);
+      }
+      sched_ring<8 * kNB, 1, kDm>();
+    } else {
+      qk();
+    }
 
     // ---- online softmax (log2 domain, lazy rescale) ----
     // Fast path: exponentiate against the running max without looking for the
@@ -342,7 +458,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (sm.kbad[buf][key]) s[kb][i] = -INFINITY;
+            if (kbad_cur[key]) s[kb][i] = -INFINITY;
           }
       }
       float mx = s[0][0];
@@ -405,6 +521,10 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  for (int32_t kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    step(kt, sm.ks[buf], sm.vs[buf], sm.kbad[buf], sm.ks[buf ^ 1], sm.vs[buf ^ 1], sm.kbad[buf ^ 1]);
   }
 
   const float l_tot = half_swap_sum(l_run);
@@ -649,6 +769,10 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
   PF_REQUIRE(n_keys >= 1, PF_ERR_SHAPE, "the context has no keys");
   PF_REQUIRE(n_keys < (int64_t{1} << 31) - kBN, PF_ERR_UNSUPPORTED, "too many keys (%lld)",
              static_cast<long long>(n_keys));
+  // pool rows are addressed with 32-bit byte offsets from the pool's start
+  const int64_t pool_rows = n_sel > 0 ? static_cast<int64_t>(n_blocks) * n_c : 0;
+  PF_REQUIRE(pool_rows * n_heads * D * 2 < (int64_t{1} << 31), PF_ERR_UNSUPPORTED,
+             "the pool holds 2 GiB or more of K (or V)");
   const int64_t num_qtiles = (n_q + kBM - 1) / kBM;
   PF_REQUIRE(num_qtiles * n_heads < 0x7FFFFFFF, PF_ERR_UNSUPPORTED, "too many query tiles");
 

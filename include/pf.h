@@ -251,7 +251,10 @@ pf_status pf_rope_shift_batched(pf_bf16* k, int64_t k_batch_stride, int n_heads,
  *   workspace            device scratch of pf_partition_attn_workspace_bytes(...)
  *                        bytes (may be NULL when that is 0).
  * Limits: 1 <= n_heads <= PF_MAX_HEADS, n_q >= 1, 0 <= n_sel <= PF_MAX_SELECTED,
- *         n_sel <= n_blocks, the total key count must be >= 1 and < 2^31.
+ *         n_sel <= n_blocks, the total key count must be >= 1 and < 2^31,
+ *         and each K/V partition (sink, pool, recent, current) must span
+ *         less than 2 GiB (tiles are read with 32-bit offsets);
+ *         PF_ERR_UNSUPPORTED otherwise.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; the online softmax is
  * fp32; probabilities are rounded to bf16 before the P.V product.
  * ------------------------------------------------------------------------- */
