@@ -149,6 +149,11 @@ def test_attn_validation(pf):
     assert _err(pf, _attn(pf, rk=B + 4))[0] == "PF_ERR_MISALIGNED"
     assert _err(pf, _attn(pf, lse=A + 2))[0] == "PF_ERR_MISALIGNED"
     assert _err(pf, _attn(pf, ns=1 << 31))[0] == "PF_ERR_UNSUPPORTED"
+    # the pool is addressed with 32-bit byte offsets: under 2 GiB of K (or V)
+    rows_2gib = (1 << 31) // (12 * 128 * 2)
+    name, msg = _err(pf, _attn(pf, nb=rows_2gib // 182 + 1))
+    assert name == "PF_ERR_UNSUPPORTED" and "pool" in msg
+    assert _err(pf, _attn(pf, nb=rows_2gib // 182 - 1, ws=None))[0] == "PF_ERR_WORKSPACE"   # passes the pool check
     need = pf.lib.pf_partition_attn_workspace_bytes(6240, 12, 27872)
     assert need > 0
     name, msg = _err(pf, _attn(pf, ws=None, wsb=0))

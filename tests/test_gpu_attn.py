@@ -114,6 +114,26 @@ def test_attn_invalid_ids_are_masked():
     assert mx <= MAX_ABS and rel <= REL_L2
 
 
+def test_attn_invalid_ids_in_whole_mid_tiles():
+    # At C1 sizes 22 key tiles hold mid rows only; their loads resolve rows through the
+    # ids. Two invalid ids fall inside such tiles: their rows are masked, as if absent.
+    say("test_attn_invalid_ids_in_whole_mid_tiles")
+    cfg = pfgen.C1
+    c = pfgen.make(cfg)
+    ids = list(range(0, 2 * cfg.top_k, 2))
+    ids[3], ids[9] = -1, cfg.pool_blocks + 7
+    valid = [i for i in ids if 0 <= i < cfg.pool_blocks]
+    o, lse = _run(c, cfg.n_c, ids)
+    rows = _sample_rows(cfg.n, 5, extra=16)
+    ks, vs = O.partitions(c, cfg.n_c, valid)
+    ref, ref_lse = O.attn_partitioned(c["q"][rows], ks, vs)
+    mx, mean, rel = attn_errors(o[rows], ref)
+    lse_err = float(np.max(np.abs(lse[:, rows] - ref_lse)))
+    say(f"  attn C1 with 2 invalid ids: max-abs {mx:.3e} mean-abs {mean:.3e} rel-L2 {rel:.3e} lse {lse_err:.2e}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2
+    assert lse_err <= 1e-3
+
+
 def test_attn_gather_equals_copy():
     # reading the pool through ids == attending over the copied rows as a partition
     say("test_attn_gather_equals_copy")
