@@ -13,13 +13,14 @@
 //    feeds 256 queries.
 //  * The MFMA operands read from LDS run kRing-1 MFMAs ahead of their use
 //    (an operand ring), so no MFMA waits on the LDS latency of its own read.
-//  * Keys stream in tiles of 128 straight from global memory into LDS
-//    (global_load_lds, 16 bytes per lane, no register staging), double
-//    buffered. Each 256-byte LDS row holds one key's 128 dims with its 16-byte
-//    chunks XOR-swizzled by the row, so the K reads (16 bytes per lane) and the
-//    transposing V reads (8 bytes per lane) hit distinct banks. Tiles inside a
-//    contiguous partition take a uniform fast path; tiles in the mid blocks or
-//    at the end resolve each row.
+//  * Keys stream in tiles of 128 straight from global memory into LDS (raw
+//    buffer loads, 16 bytes per lane, no register staging), double buffered.
+//    Each 256-byte LDS row holds one key's 128 dims with its 16-byte chunks
+//    XOR-swizzled by the row, so the K reads (16 bytes per lane) and the
+//    transposing V reads (8 bytes per lane) hit distinct banks. The next
+//    tile's loads are spread over the current tile's QK MFMAs when the tile
+//    lies in one partition or holds mid keys only; a tile across a partition
+//    boundary resolves each row and loads in one burst.
 //  * The score tile is computed transposed, S^T = K Q^T, so each lane holds
 //    half of one query's 128 scores and the other half-wave the rest: the row
 //    max needs one swap between half-waves, the row sum none, and the
