@@ -101,6 +101,7 @@ struct AttnArgs {
   int32_t n_tail;           // units cut into key segments (after the whole rounds)
   int32_t n_seg;            // segments per cut unit (1: the tail units run whole)
   float scale_log2;
+  float inv_nc;             // 1 / n_c
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -145,6 +146,19 @@ struct TileSrc {
   int voff[kLoadsPerWave];
 };
 
+// x / n_c for a mid key's offset x (0 <= x < n_sel * n_c, so the quotient is
+// below PF_MAX_SELECTED): an fp32 estimate is within one of the quotient, and
+// one correction step fixes it. (Integer division has no instruction here.)
+__device__ __forceinline__ int32_t mid_block(int32_t x, int32_t n_c, float inv_nc) {
+  int32_t q = static_cast<int32_t>(static_cast<float>(x) * inv_nc);
+  const int32_t r = x - q * n_c;
+  if (r < 0)
+    --q;
+  else if (r >= n_c)
+    ++q;
+  return q;
+}
+
 // Tile inside one contiguous partition (sink, recent or current).
 __device__ __forceinline__ bool contiguous_tile(const AttnArgs& a, int h, int32_t kt, int wave_u, int lane,
                                                 TileSrc& t) {
@@ -187,7 +201,7 @@ __device__ __forceinline__ bool mid_tile(const AttnArgs& a, const int32_t* ids_l
   for (int i = 0; i < kLoadsPerWave; ++i) {
     const int row = tile_row(wave_u, lane, i);
     const int32_t x = k0 + row - a.e_sink;
-    const int32_t b = x / a.n_c;
+    const int32_t b = mid_block(x, a.n_c, a.inv_nc);
     const int32_t id = ids_lds[b];
     const bool ok = id >= 0 && id < a.n_blocks;
     const int64_t prow = ok ? static_cast<int64_t>(id) * a.n_c + (x - b * a.n_c) : 0;
@@ -233,7 +247,7 @@ __device__ __forceinline__ void load_general(const AttnArgs& a, const int32_t* i
       pt = 0; prow = kk - b_sink;
     } else if (kk < a.e_mid) {
       const int32_t x = kk - a.e_sink;
-      const int32_t b = x / a.n_c;
+      const int32_t b = mid_block(x, a.n_c, a.inv_nc);
       const int32_t id = ids_lds[b];
       if (id >= 0 && id < a.n_blocks) {
         pt = 1; prow = static_cast<int64_t>(id) * a.n_c + (x - b * a.n_c);
@@ -813,6 +827,7 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
   a.row_stride = static_cast<int64_t>(n_heads) * D;
   a.H = n_heads;
   a.n_c = n_sel > 0 ? n_c : 1;
+  a.inv_nc = 1.0f / static_cast<float>(a.n_c);
   a.n_sel = n_sel;
   a.n_blocks = n_blocks;
   a.e_sink = static_cast<int32_t>(n_sink);
