@@ -288,10 +288,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       __syncthreads();
     }
   }
-  if (threadIdx.x < top_k) chosen[threadIdx.x] = static_cast<uint32_t>(keys[threadIdx.x] & 0xFFFFFFFFu);
+  const int tid = static_cast<int>(threadIdx.x);
+  if (tid < top_k) chosen[tid] = static_cast<uint32_t>(keys[tid] & 0xFFFFFFFFu);
   __syncthreads();
-  if (threadIdx.x < top_k) {
-    const uint32_t me = chosen[threadIdx.x];
+  if (tid < top_k) {
+    const uint32_t me = chosen[tid];
     int rank = 0;
     for (int r = 0; r < top_k; ++r) rank += chosen[r] < me;
     ids[rank] = static_cast<int32_t>(me);
@@ -299,9 +300,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
   if (tags == nullptr) return;
   __syncthreads();
-  if (threadIdx.x < top_k)
-    place_one(sorted_ids[threadIdx.x], threadIdx.x, top_k, tags + b * n_blocks, n_blocks, recent_first_frame,
-              block_frames, deltas + b * top_k + threadIdx.x);
+  if (tid < top_k)
+    place_one(sorted_ids[tid], tid, top_k, tags + b * n_blocks, n_blocks, recent_first_frame, block_frames,
+              deltas + b * top_k + tid);
 }
 
 // Placement, one workgroup per cache.
