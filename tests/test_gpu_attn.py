@@ -170,6 +170,18 @@ def test_attn_head_count_limits(H):
     _compare(c, 11, [5, 1, 3], rows=_sample_rows(n_q, H), label=f"H={H}")
 
 
+def test_attn_32_heads_whole_partition_and_mid_tiles():
+    # 32 heads (row stride 8 KB) with partitions long enough that whole key tiles lie
+    # inside the sink, inside the mid blocks and inside recent/current: every loader path
+    say("test_attn_32_heads_whole_partition_and_mid_tiles")
+    rng = np.random.default_rng(41)
+    H, n_c, n_q = 32, 160, 300
+    c = dict(q=_bits(rng, n_q, H), sink_k=_bits(rng, 640, H), sink_v=_bits(rng, 640, H),
+             pool_k=_bits(rng, 6 * n_c, H), pool_v=_bits(rng, 6 * n_c, H), recent_k=_bits(rng, 300, H),
+             recent_v=_bits(rng, 300, H), cur_k=_bits(rng, 400, H), cur_v=_bits(rng, 400, H))
+    _compare(c, n_c, [4, 0, 5, 2], rows=_sample_rows(n_q, 41, extra=8), label="H=32, 1,980 keys")
+
+
 def test_attn_max_selected_blocks_duplicates_and_scale():
     say("test_attn_max_selected_blocks_duplicates_and_scale")
     rng = np.random.default_rng(31)
