@@ -647,6 +647,16 @@ extern "C" size_t pf_hr_branch_workspace_bytes(int n_batch, int T, int H, int W,
   return make_branch_plan(n_batch, T, H, W, c_in, widths, hidden).ws_bytes;
 }
 
+extern "C" int64_t pf_hr_branch_out_tokens(int T, int H, int W) {
+  if (T < 2 || H < 8 || W < 8) return 0;
+  int t = T, h = H, w = W;
+  for (int s = 0; s < PF_HR_STAGES; ++s) {
+    const int kt = s == 0 ? 2 : 1, k = s == 0 ? 1 : 2;
+    t /= kt; h /= k; w /= k;
+  }
+  return static_cast<int64_t>(t) * h * w;
+}
+
 extern "C" pf_status pf_hr_branch(const pf_bf16* z, int n_batch, int T, int H, int W, int c_in,
                                   const pf_bf16* const* stage_w, const float* const* stage_b, const int* widths,
                                   const pf_bf16* proj_w, const float* proj_b, int hidden, pf_bf16* out,

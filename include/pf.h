@@ -106,9 +106,10 @@ pf_status pf_score_select(const pf_bf16* q, int64_t n_q, int n_heads,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Sub-sampled scoring: the same score computed from query rows 0, q_step,
- * 2*q_step, ... and heads 0, head_step, 2*head_step, ... only. The pages speed
- * selection up by scoring with part of the queries and half of the heads
- * [arXiv HTML, "Implementation Details"]; q_step = head_step = 1 is
+ * 2*q_step, ... and heads 0, head_step, 2*head_step, ... only. The pages run
+ * selection only at each block's first denoising step [digest, 方法步骤详情 (3)]
+ * and speed it up further by scoring with a subsample of the query tokens and
+ * half of the attention heads [digest, 局限与改进]; q_step = head_step = 1 is
  * pf_score_select. The means run over the rows and heads that are used.
  * Limits as pf_score_select, plus q_step >= 1 and 1 <= head_step <= n_heads. */
 size_t pf_score_select_sub_workspace_bytes(int64_t n_q, int n_heads, int q_step, int head_step, int n_blocks,
@@ -252,9 +253,11 @@ pf_status pf_rope_shift_batched(pf_bf16* k, int64_t k_batch_stride, int n_heads,
  *                        bytes (may be NULL when that is 0).
  * Limits: 1 <= n_heads <= PF_MAX_HEADS, n_q >= 1, 0 <= n_sel <= PF_MAX_SELECTED,
  *         n_sel <= n_blocks, the total key count must be >= 1 and < 2^31,
- *         and each K/V partition (sink, pool, recent, current) must span
- *         less than 2 GiB (tiles are read with 32-bit offsets);
- *         PF_ERR_UNSUPPORTED otherwise.
+ *         and the pool's K (and V) must span less than 2 GiB, because its
+ *         rows, scattered by mid_ids, are addressed with 32-bit byte offsets
+ *         from the pool's start; PF_ERR_UNSUPPORTED otherwise. The sink,
+ *         recent and current partitions may be larger: their tiles are
+ *         addressed from each tile's own first row.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; the online softmax is
  * fp32; probabilities are rounded to bf16 before the P.V product.
  * ------------------------------------------------------------------------- */
@@ -335,6 +338,12 @@ pf_status pf_hr_conv(const pf_bf16* x, int n_batch, int T, int H, int W, int c_i
                      void* workspace, size_t workspace_bytes, void* stream);
 
 size_t pf_hr_branch_workspace_bytes(int n_batch, int T, int H, int W, int c_in, const int* widths, int hidden);
+
+/* Tokens per block that pf_hr_branch writes for a T x H x W latent block:
+ * the product of the dimensions left after the stages' kernels, which is
+ * N_c = floor(T/2) floor(H/8) floor(W/8); 0 when the block is smaller than
+ * 2 x 8 x 8. The caller sizes `out` as [n_batch][this][hidden]. */
+int64_t pf_hr_branch_out_tokens(int T, int H, int W);
 
 pf_status pf_hr_branch(const pf_bf16* z, int n_batch, int T, int H, int W, int c_in,
                        const pf_bf16* const* stage_w, const float* const* stage_b, const int* widths,

@@ -179,9 +179,9 @@ def block_scores(q_bits: np.ndarray, pool_k_bits: np.ndarray, n_c: int, q_step: 
                  head_step: int = 1) -> np.ndarray:
     """s_j = (1/H) sum_h <mean_i q_{i,h}, mean_{t in block j} k_{t,h}> / sqrt(128).
 
-    q_step / head_step > 1: the pages' faster selection ([arXiv] "Implementation
-    Details"): only query rows 0, q_step, ... and heads 0, head_step, ... enter,
-    and the means run over those.
+    q_step / head_step > 1: the pages' faster selection ([digest] 局限与改进:
+    subsampled query tokens and half of the heads): only query rows 0, q_step,
+    ... and heads 0, head_step, ... enter, and the means run over those.
     """
     q = bf16_to_f64(q_bits)[::q_step, ::head_step]          # [n_q', H', D]
     H = q.shape[1]

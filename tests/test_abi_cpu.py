@@ -154,6 +154,15 @@ def test_attn_validation(pf):
     name, msg = _err(pf, _attn(pf, nb=rows_2gib // 182 + 1))
     assert name == "PF_ERR_UNSUPPORTED" and "pool" in msg
     assert _err(pf, _attn(pf, nb=rows_2gib // 182 - 1, ws=None))[0] == "PF_ERR_WORKSPACE"   # passes the pool check
+    # contiguous partitions of 2 GiB or more are accepted (their tiles are
+    # addressed from each tile's first row): the call gets past every shape
+    # check and stops at the missing workspace, before any launch
+    for part in ("ns", "nr", "ncur"):
+        big = dict(ns=12480, nr=6240, ncur=6240)
+        big[part] = rows_2gib + 1000
+        n_keys = big["ns"] + 16 * 182 + big["nr"] + big["ncur"]
+        assert pf.lib.pf_partition_attn_workspace_bytes(6240, 12, n_keys) > 0
+        assert _err(pf, _attn(pf, ws=None, wsb=0, **big))[0] == "PF_ERR_WORKSPACE", part
     need = pf.lib.pf_partition_attn_workspace_bytes(6240, 12, 27872)
     assert need > 0
     name, msg = _err(pf, _attn(pf, ws=None, wsb=0))
@@ -216,6 +225,11 @@ def test_hr_branch_validation(pf):
     name, msg = _err(pf, call(wsb=need - 1))
     assert name == "PF_ERR_WORKSPACE" and str(need) in msg
     assert _err(pf, call(wsp=None))[0] == "PF_ERR_WORKSPACE"
+    # the output size the binding allocates comes from the library: the
+    # default block gives the pages' 182 tokens
+    assert L.pf_hr_branch_out_tokens(4, 60, 104) == 182
+    assert L.pf_hr_branch_out_tokens(5, 63, 111) == 2 * 7 * 13
+    assert L.pf_hr_branch_out_tokens(1, 60, 104) == 0
 
 
 def test_select_place_validation(pf):
@@ -228,3 +242,95 @@ def test_select_place_validation(pf):
     assert _err(pf, call(tags=C + 2))[0] == "PF_ERR_MISALIGNED"
     assert _err(pf, call(top_k=41))[0] == "PF_ERR_RANGE"
     assert _err(pf, call(ws=None))[0] == "PF_ERR_WORKSPACE"
+
+
+class _FakeDev:
+    """Stands in for a device tensor in the binding's host-side checks: the
+    attributes those checks read, backed by a CPU tensor. No call gets as far
+    as the library, so nothing is ever dereferenced."""
+
+    def __init__(self, t, device="cuda:0"):
+        import torch
+        self._t = t
+        self.is_cuda = True
+        self.device = torch.device(device)
+        self.dtype = t.dtype
+        self.shape = t.shape
+
+    def dim(self):
+        return self._t.dim()
+
+    def numel(self):
+        return self._t.numel()
+
+    def element_size(self):
+        return self._t.element_size()
+
+    def is_contiguous(self):
+        return self._t.is_contiguous()
+
+    def stride(self, *a):
+        return self._t.stride(*a)
+
+    def __getitem__(self, i):
+        return _FakeDev(self._t[i], str(self.device))
+
+    def data_ptr(self):
+        raise AssertionError("the binding must reject this call before passing pointers")
+
+
+def _fake(shape, dtype=None, device="cuda:0"):
+    import torch
+    return _FakeDev(torch.zeros(shape, dtype=dtype or torch.bfloat16), device)
+
+
+def test_binding_checks_attention_outputs(pf):
+    import torch
+    H, n = 2, 64
+    q = _fake((n, H, 128))
+    kv = _fake((32, H, 128))
+    call = lambda **k: pf.pf_partition_attn(q, kv, kv, None, None, 8, None, kv, kv, kv, kv, **k)
+    with pytest.raises(ValueError, match="shape"):
+        call(o=_fake((n - 1, H, 128)))                         # one row short
+    with pytest.raises(TypeError):
+        call(o=_fake((n, H, 128), torch.float32))              # wrong dtype
+    with pytest.raises(ValueError, match="CUDA"):
+        call(o=torch.zeros((n, H, 128), dtype=torch.bfloat16))  # host buffer
+    with pytest.raises(ValueError, match="cuda:1"):
+        call(o=_fake((n, H, 128), device="cuda:1"))            # another device
+    with pytest.raises(ValueError, match="lse"):
+        call(o=_fake((n, H, 128)), lse=_fake((H, n - 1), torch.float32))
+    with pytest.raises(TypeError, match="lse"):
+        call(o=_fake((n, H, 128)), lse=_fake((H, n), torch.float16))
+    with pytest.raises(TypeError, match="workspace"):
+        call(o=_fake((n, H, 128)), workspace=torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="recent_k"):
+        pf.pf_partition_attn(q, kv, kv, None, None, 8, None, _fake((32, H, 128), device="cuda:1"), kv, kv, kv)
+
+
+def test_binding_checks_selection_outputs(pf):
+    import torch
+    H, n, n_c, M, k = 2, 64, 8, 10, 4
+    q = _fake((n, H, 128))
+    pool = _fake((M * n_c, H, 128))
+    tags = _fake((M,), torch.int32)
+    with pytest.raises(ValueError, match="ids_out"):
+        pf.pf_score_select(q, pool, n_c, k, ids_out=_fake((k - 1,), torch.int32))
+    with pytest.raises(ValueError, match="scores_out"):
+        pf.pf_score_select(q, pool, n_c, k, ids_out=_fake((k,), torch.int32),
+                           scores_out=_fake((M - 1,), torch.float32))
+    with pytest.raises(TypeError, match="scores_out"):
+        pf.pf_score_select(q, pool, n_c, k, ids_out=_fake((k,), torch.int32), scores_out=_fake((M,), torch.int32))
+    with pytest.raises(TypeError, match="ids_out"):
+        pf.pf_select_place(q, pool, n_c, k, tags, 48, 4, ids_out=torch.zeros(k, dtype=torch.int32))
+    with pytest.raises(ValueError, match="deltas_out"):
+        pf.pf_select_place(q, pool, n_c, k, tags, 48, 4, ids_out=_fake((k,), torch.int32),
+                           deltas_out=_fake((k - 1,), torch.int32))
+    with pytest.raises(ValueError, match="pos_tags"):
+        pf.pf_select_place(q, pool, n_c, k, _fake((M,), torch.int32, "cuda:1"), 48, 4)
+    qb = _fake((3, n, H, 128))
+    pb = _fake((3, M * n_c, H, 128))
+    with pytest.raises(ValueError, match="ids_out"):
+        pf.pf_score_select_batched(qb, pb, n_c, k, ids_out=_fake((3, k - 1), torch.int32))
+    with pytest.raises(ValueError, match="deltas_out"):
+        pf.pf_selection_deltas(_fake((k,), torch.int32), tags, 48, 4, deltas_out=_fake((k - 1,), torch.int32))

@@ -233,3 +233,44 @@ def test_attn_late_dominant_keys(boost):
              recent_k=_bits(rng, 500, H, 0.3), recent_v=_bits(rng, 500, H),
              cur_k=O.f64_to_bf16(cur), cur_v=_bits(rng, 400, H))
     _compare(c, 20, [1, 3], label=f"late keys +{boost} nats")
+
+
+def test_attn_and_select_on_a_side_stream_without_workspace():
+    # the binding allocates the workspace and outputs while the kernels run on
+    # a stream other than the current one; memory the current stream allocates
+    # and overwrites right after the calls must not be the memory those kernels
+    # still use
+    say("test_attn_and_select_on_a_side_stream_without_workspace")
+    cfg = pfgen.C1
+    c = pfgen.make(cfg)
+    ids = sorted(np.random.default_rng(5).choice(cfg.pool_blocks, cfg.top_k, replace=False).tolist())
+    t = {k: dev(v) for k, v in c.items()}
+    mid = dev_i32(ids)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    need = pf.pf_partition_attn_workspace_bytes(cfg.n, cfg.heads, cfg.n_keys)
+    assert need > 0
+    o, lse = pf.pf_partition_attn(t["q"], t["sink_k"], t["sink_v"], t["pool_k"], t["pool_v"], cfg.n_c, mid,
+                                  t["recent_k"], t["recent_v"], t["cur_k"], t["cur_v"], want_lse=True, stream=side)
+    sel, scores = pf.pf_score_select(t["q"], t["pool_k"], cfg.n_c, cfg.top_k, stream=side)
+    junk = [torch.full((need,), 255, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    junk += [torch.full(tuple(o.shape), -7, dtype=torch.int16, device="cuda") for _ in range(2)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    rows = _sample_rows(cfg.n, 9, extra=16)
+    ks, vs = O.partitions(c, cfg.n_c, ids)
+    ref, ref_lse = O.attn_partitioned(c["q"][rows], ks, vs)
+    mx, mean, rel = attn_errors(host(o)[rows], ref)
+    say(f"  side stream: max-abs {mx:.3e} rel-L2 {rel:.3e}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2
+    assert float(np.max(np.abs(lse.cpu().numpy()[:, rows] - ref_lse))) <= 1e-3
+    s_ref = O.block_scores(c["q"], c["pool_k"], cfg.n_c)
+    got = sel.cpu().numpy().tolist()
+    err = float(np.max(np.abs(scores.cpu().numpy().astype(np.float64) - s_ref)))
+    assert err <= 1e-5 + 1e-5 * float(np.max(np.abs(s_ref)))
+    if O.topk_gap(s_ref, cfg.top_k) < 1e-3:      # flagged: any set within the margin
+        assert O.topk_acceptable(got, s_ref, cfg.top_k, 1e-3)
+    else:
+        assert got == O.select_topk(s_ref, cfg.top_k)
+    del junk

@@ -51,6 +51,74 @@ def test_closed_form_rotation():
         assert np.count_nonzero(r) == 2
 
 
+def _measured_freqs(axis_start, n_pairs, axis):
+    """Angle per unit position of each pair of one axis, read off the encoder:
+    a unit vector in pair j encoded at position 1 of that axis comes back as
+    (cos a_j, sin a_j), and a_j in (0, 1] is recovered with atan2."""
+    out = np.empty(n_pairs)
+    for j in range(n_pairs):
+        e = np.zeros(O.HEAD_DIM)
+        e[axis_start + 2 * j] = 1.0
+        pos = [0.0, 0.0, 0.0]
+        pos[axis] = 1.0
+        r = O.rope_encode(e, *pos)
+        out[j] = math.atan2(r[axis_start + 2 * j + 1], r[axis_start + 2 * j])
+    return out
+
+
+def _check_roformer_table(th, n_dims):
+    """Properties of theta_j = 10000^(-2j/n_dims) that pin every entry without
+    restating the power: theta_0 = 1; theta_j * theta_{n/2 - j} = 10000^-1 for
+    the pairs that exist; consecutive ratios are all equal, and the (n/2)-th
+    power of that ratio is 10000^-1 (a geometric table ending one step short
+    of 1e-4)."""
+    half = n_dims // 2
+    assert th[0] == pytest.approx(1.0, abs=1e-15)
+    for j in range(1, half):
+        if half - j < len(th):
+            assert th[j] * th[half - j] == pytest.approx(1e-4, rel=1e-12), j
+    ratios = th[1:] / th[:-1]
+    assert np.max(np.abs(ratios - ratios[0])) < 1e-12
+    assert ratios[0] ** half == pytest.approx(1e-4, rel=1e-12)
+
+
+def test_temporal_frequency_table():
+    # [digest] 前置知识 RoPE and [arXiv] "The Position Misalignment Problem":
+    # theta_t spans 44 dims = 22 pairs; the RoFormer table gives theta_{t,11} =
+    # 10000^(-1/2) = 0.01 exactly, so position 100 turns pair 11 by one radian
+    th = _measured_freqs(0, 22, 0)
+    _check_roformer_table(th, 44)
+    assert th[11] == pytest.approx(0.01, rel=1e-13)
+    e = np.zeros(O.HEAD_DIM)
+    e[22] = 1.0
+    r = O.rope_encode(e, 100.0, 0.0, 0.0)
+    assert r[22] == pytest.approx(math.cos(1.0), abs=1e-13)
+    assert r[23] == pytest.approx(math.sin(1.0), abs=1e-13)
+
+
+def test_height_width_frequency_tables():
+    # 42 dims = 21 pairs each; theta_7 = 10000^(-1/3), so its cube is 1e-4
+    for start, axis in ((44, 1), (86, 2)):
+        th = _measured_freqs(start, 21, axis)
+        _check_roformer_table(th, 42)
+        assert th[7] ** 3 == pytest.approx(1e-4, rel=1e-12)
+
+
+def test_planted_frequency_exponent_fails_the_table(monkeypatch):
+    # an exponent of -j/d instead of -2j/d (and one with the axis width
+    # swapped) must each break a table pin, although theta_0 = 1 still holds
+    import oracle.pf_oracle as impl
+    mutants = [lambda d, base=O.ROPE_BASE: base ** (-np.arange(d // 2, dtype=np.float64) / d),
+               lambda d, base=O.ROPE_BASE: base ** (-2.0 * np.arange(d // 2, dtype=np.float64) / 128)]
+    for mut in mutants:
+        with monkeypatch.context() as m:
+            m.setattr(impl, "axis_freqs", mut)
+            with pytest.raises(AssertionError):
+                _check_roformer_table(_measured_freqs(0, 22, 0), 44)
+    # the unpatched table passes the same check
+    _check_roformer_table(_measured_freqs(0, 22, 0), 44)
+
+
 def test_relative_position_property():
     # Textbook RoPE: <enc(q, p1), enc(k, p2)> depends only on p1 - p2 per axis.
     rng = np.random.default_rng(3)
