@@ -216,6 +216,61 @@ def topk_acceptable(ids: Sequence[int], scores: Sequence[float], k: int, tol: fl
 
 
 # ---------------------------------------------------------------------------
+# Baseline selectors  [digest] 实验结果 (dynamic selection against FIFO and
+# random selection); [arXiv] "FIFO vs. Dynamic Context Selection"
+# ---------------------------------------------------------------------------
+#
+# Readings: FIFO keeps the k most recent pool blocks (the highest ids, since
+# blocks enter the pool in arrival order). Random selection draws k distinct
+# blocks uniformly; the pages name no generator, so the draws come from
+# SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+# generators", OOPSLA 2014) used as a counter-based stream, and the k-subset
+# from Floyd's sampling algorithm (Bentley and Floyd, "A sample of
+# brilliance", CACM 1987).
+
+_M64 = (1 << 64) - 1
+SPLITMIX_GAMMA = 0x9E3779B97F4A7C15
+
+
+def splitmix64_mix(z: int) -> int:
+    """The SplitMix64 output function of a 64-bit state."""
+    z &= _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def random_draw(seed: int, counter: int, i: int) -> int:
+    """Draw i (1, 2, ...) of stream (seed, counter): SplitMix64 started from
+    state seed + counter * 2^32 * gamma, i.e. mix(seed + (counter * 2^32 + i) * gamma)."""
+    return splitmix64_mix((seed + ((counter << 32) + i) * SPLITMIX_GAMMA) & _M64)
+
+
+def floyd_sample(n: int, k: int, draw) -> List[int]:
+    """Floyd's algorithm: k distinct values of range(n), each k-subset equally
+    likely when draw(r, j) is uniform on 0..j. Step r (r = 0..k-1) takes
+    j = n - k + r and t = draw(r, j); it keeps t unless t was already kept,
+    in which case it keeps j. Returned in ascending order."""
+    kept = set()
+    for r in range(k):
+        j = n - k + r
+        t = draw(r, j)
+        kept.add(j if t in kept else t)
+    return sorted(kept)
+
+
+def select_random(n_blocks: int, k: int, seed: int, counter: int) -> List[int]:
+    """k distinct pool blocks chosen at random (the random-selection baseline);
+    step r maps draw r+1 to 0..j by the top 32 bits times (j+1), over 2^32."""
+    return floyd_sample(n_blocks, k, lambda r, j: ((random_draw(seed, counter, r + 1) >> 32) * (j + 1)) >> 32)
+
+
+def select_fifo(n_blocks: int, k: int) -> List[int]:
+    """The FIFO baseline: the k most recent pool blocks."""
+    return list(range(n_blocks - k, n_blocks))
+
+
+# ---------------------------------------------------------------------------
 # Placement of the selected blocks  [arXiv] "The Position Misalignment Problem",
 # "Incremental RoPE adjustment"; [summary] "Method" (remaining tokens shifted to
 # continuous indices)

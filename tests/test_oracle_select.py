@@ -144,3 +144,67 @@ def test_subsampled_scores_closed_forms():
     q2 = O.f64_to_bf16(q2)
     assert np.allclose(O.block_scores(q2, pk, n_c, head_step=2), 2 * O.block_scores(q2, pk, n_c), rtol=1e-12,
                        atol=1e-15)
+
+
+# ---- baseline selectors ([digest] 实验结果; [arXiv] "FIFO vs. Dynamic Context Selection") ----
+
+def test_splitmix64_published_outputs():
+    # the first outputs of SplitMix64 seeded with 0, as its reference
+    # implementation prints them; draw i of stream (0, 0) is output i
+    want = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    assert [O.random_draw(0, 0, i) for i in (1, 2, 3)] == want
+
+
+def _all_draw_sequences(n, k):
+    import itertools
+    return itertools.product(*[range(n - k + r + 1) for r in range(k)])
+
+
+@pytest.mark.parametrize("n,k", [(6, 3), (5, 1), (7, 2), (4, 4)])
+def test_floyd_sampling_is_exactly_uniform(n, k):
+    # with every step's draw ranging over all of 0..j, each k-subset comes out
+    # the same number of times: (n!/(n-k)!) / C(n, k) = k!
+    from collections import Counter
+    from math import comb, factorial
+    counts = Counter()
+    for seq in _all_draw_sequences(n, k):
+        sub = O.floyd_sample(n, k, lambda r, j, seq=seq: seq[r])
+        assert len(sub) == k and sub == sorted(set(sub)) and all(0 <= x < n for x in sub)
+        counts[tuple(sub)] += 1
+    assert len(counts) == comb(n, k)
+    assert set(counts.values()) == {factorial(k)}
+
+
+def test_floyd_planted_mistake_breaks_uniformity():
+    # keeping t when it is already present (a lost sample) or drawing from
+    # 0..j-1 both break the exact count
+    from collections import Counter
+
+    def floyd_wrong_range(n, k, draw):
+        kept = set()
+        for r in range(k):
+            j = n - k + r
+            t = draw(r, j) % j if j else 0
+            kept.add(j if t in kept else t)
+        return sorted(kept)
+    counts = Counter(tuple(floyd_wrong_range(6, 3, lambda r, j, s=s: s[r])) for s in _all_draw_sequences(6, 3))
+    assert len(set(counts.values())) > 1
+
+
+def test_select_random_properties():
+    M, k = 40, 16
+    seen = np.zeros(M)
+    for counter in range(3000):
+        ids = O.select_random(M, k, 1234, counter)
+        assert len(ids) == k and ids == sorted(set(ids)) and 0 <= ids[0] and ids[-1] < M
+        seen[ids] += 1
+    # each block is chosen with probability k/M: 1200 of 3000, sd ~ 26.8
+    assert np.max(np.abs(seen - 3000 * k / M)) < 5 * np.sqrt(3000 * (k / M) * (1 - k / M))
+    assert O.select_random(M, M, 7, 0) == list(range(M))
+    assert O.select_random(M, k, 7, 0) != O.select_random(M, k, 7, 1)
+    assert O.select_random(M, k, 7, 0) == O.select_random(M, k, 7, 0)
+
+
+def test_select_fifo_keeps_the_newest_blocks():
+    assert O.select_fifo(40, 16) == list(range(24, 40))
+    assert O.select_fifo(16, 16) == list(range(16))
