@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--batched-only", action="store_true",
                     help="only run the batched selection/RoPE measurement (for its own profile)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-c4", action="store_true", help="skip the unbounded 748,800-key contrast")
+    ap.add_argument("--layer-step-only", action="store_true",
+                    help="only the warm-up and timed layer-steps (for profiling their kernels)")
     ap.add_argument("--hr-only", action="store_true",
                     help="time only the HR-branch compressor (for profiling its kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -53,6 +56,13 @@ def parse():
 
 def attn_flops(n_q, n_k, heads):
     return 4.0 * n_q * n_k * 128 * heads
+
+
+def stats(ms):
+    """Mean, median and the 10th / 90th percentiles of per-launch times (ms)."""
+    ms = np.asarray(ms, dtype=np.float64)
+    return {"n": int(ms.size), "mean": round(float(ms.mean()), 5), "median": round(float(np.median(ms)), 5),
+            "p10": round(float(np.percentile(ms, 10)), 5), "p90": round(float(np.percentile(ms, 90)), 5)}
 
 
 def kernel_source_sha(text=None):
@@ -78,39 +88,90 @@ def traffic_from_counters():
     return d.get("hbm_bytes_per_launch")
 
 
+def host_info():
+    """CPU model, usable cores and numpy's BLAS, for the CPU figures."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                       if i.get("user_api") == "blas"})
+    except Exception:  # noqa: BLE001 - informational only
+        blas = []
+    return {"cpu_model": model, "cores": len(os.sched_getaffinity(0)), "blas": ", ".join(blas) or "unknown"}
+
+
+def _oracle_attention_pool(O, q, ks, vs, workers, chunk=256):
+    """The oracle's attention on every (head, 256-query chunk) as its own task,
+    over a thread pool, each task's BLAS on one thread."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    n_q, H = q.shape[0], q.shape[1]
+    tasks = [(h, r0) for h in range(H) for r0 in range(0, n_q, chunk)]
+
+    def run(t):
+        h, r0 = t
+        O.attn_partitioned(q[r0:r0 + chunk, h:h + 1], [k[:, h:h + 1] for k in ks], [v[:, h:h + 1] for v in vs])
+
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(run, tasks))
+
+
 def cpu_baseline(cache, cfg, seconds):
-    """The oracle's layer-step on the host: whole steps repeated until about
-    `seconds` of wall time, or, if one whole step would take far longer, the
-    step restricted to its first query rows."""
+    """The oracle's layer-step on the host cores: selection, placement and the
+    RoPE shift by the oracle's own functions, then its attention split into
+    (head, 256-query chunk) tasks over a pool of one worker per usable core.
+    Whole steps repeat for about `seconds` of wall time; if one step would take
+    far longer, the attention covers only the first query rows."""
     import oracle as O
-    from threadpoolctl import threadpool_info
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    info = host_info()
+    workers = min(info["cores"], 16)    # one GPU's share of the host cores
     tags = O.initial_pos_tags(cfg.pool_blocks, cfg.sink_blocks, cfg.block_frames)
     fr = (cfg.sink_blocks + cfg.pool_blocks) * cfg.block_frames
+
+    def step(rows):
+        scores = O.block_scores(cache["q"], cache["pool_k"], cfg.n_c)
+        ids = O.select_topk(scores, cfg.top_k)
+        deltas, _ = O.placement_deltas(ids, tags, fr, cfg.block_frames)
+        pool_k = O.rope_shift_blocks(cache["pool_k"], cfg.n_c, ids, deltas)
+        ks, vs = O.partitions(dict(cache, pool_k=pool_k), cfg.n_c, ids)
+        _oracle_attention_pool(O, cache["q"][:rows], ks, vs, workers)
+
+    cal_rows = 512
     t0 = time.perf_counter()
-    O.layer_step(cache, tags, cfg.n_c, cfg.top_k, fr, cfg.block_frames, q_rows=np.arange(256))
+    step(cal_rows)
     t_cal = time.perf_counter() - t0
-    est_full = t_cal * cfg.n / 256
+    est_full = t_cal * cfg.n / cal_rows
     if est_full > 2 * seconds:          # one whole step is too long: sample query rows
-        rows = max(256, (int(cfg.n * seconds / est_full) // 64) * 64)
+        rows = max(256, (int(cfg.n * seconds / est_full) // 256) * 256)
         t0 = time.perf_counter()
-        O.layer_step(cache, tags, cfg.n_c, cfg.top_k, fr, cfg.block_frames, q_rows=np.arange(rows))
+        step(rows)
         dt = time.perf_counter() - t0
-        n_steps, what = 1, f"one layer-step restricted to the first {rows} of {cfg.n} query rows"
+        n_steps, what = 1, f"one layer-step with attention for the first {rows} of {cfg.n} query rows"
     else:
         rows, n_steps, dt = cfg.n, 0, 0.0
         while dt < seconds:
             t0 = time.perf_counter()
-            O.layer_step(cache, tags, cfg.n_c, cfg.top_k, fr, cfg.block_frames)
+            step(cfg.n)
             dt += time.perf_counter() - t0
             n_steps += 1
         what = f"{n_steps} whole layer-step(s) (all {cfg.n} query rows)"
     tflops = n_steps * attn_flops(rows, cfg.n_keys, cfg.heads) / dt / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(tflops, 4), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "sample": f"the fp64 numpy oracle on the bench workload: {what} -- scoring of all queries over "
-                      f"the {cfg.pool_blocks}-block pool, top-{cfg.top_k} selection, placement, RoPE shift "
-                      f"and attention over all {cfg.n_keys} keys; {dt:.1f} s wall; value = attention flops "
-                      f"of the sample / wall time",
+                      f"the {cfg.pool_blocks}-block pool, top-{cfg.top_k} selection, placement, RoPE shift, "
+                      f"then attention over all {cfg.n_keys} keys as (head, 256-query chunk) tasks on "
+                      f"{workers} worker threads with one BLAS thread each; {dt:.1f} s wall; value = attention "
+                      f"flops of the sample / wall time",
+            "cpu_model": info["cpu_model"], "blas": info["blas"], "threads_per_worker": 1,
             "seconds": round(dt, 2), "rows": rows, "layer_steps": n_steps}
 
 
@@ -184,11 +245,12 @@ def selection_cadence(pf, torch, pfgen, dev, ms_attn, caches=8):
     """The pages' faster selection (a quarter of the query rows, every other
     head) against full scoring: time per call on the default layer and how many
     of the 16 selected blocks agree on caches with clear block preferences
-    (per-head query mean, block-wise key offsets). A FIFO selector (the 16
-    newest blocks) is reported alongside."""
+    (per-head query mean, block-wise key offsets). The pages' two baselines are
+    reported alongside: FIFO (the 16 newest blocks) and random selection
+    (pf_select_random, one stream per cache)."""
     cfg = pfgen.C2Q
     k = cfg.top_k
-    agree_sub, agree_fifo = [], []
+    agree_sub, agree_fifo, agree_rand = [], [], []
     t_full, t_sub = [], []
     for i in range(caches):
         c = pfgen.make(cfg, cfg.seed + 100 + i)
@@ -198,6 +260,8 @@ def selection_cadence(pf, torch, pfgen, dev, ms_attn, caches=8):
         fs, ss = set(full.cpu().numpy().tolist()), set(sub.cpu().numpy().tolist())
         agree_sub.append(len(fs & ss) / k)
         agree_fifo.append(len(fs & set(range(cfg.pool_blocks - k, cfg.pool_blocks))) / k)
+        rnd = pf.pf_select_random(cfg.pool_blocks, k, 2024, i)
+        agree_rand.append(len(fs & set(rnd.cpu().numpy().tolist())) / k)
         for fn, acc in ((lambda: pf.pf_score_select(q, pk, cfg.n_c, k), t_full),
                         (lambda: pf.pf_score_select_sub(q, pk, cfg.n_c, k, 4, 2), t_sub)):
             fn()
@@ -213,6 +277,8 @@ def selection_cadence(pf, torch, pfgen, dev, ms_attn, caches=8):
             "full_ms": round(float(np.median(t_full)), 4), "subsampled_ms": round(float(np.median(t_sub)), 4),
             "subsampled_topk_agreement": round(float(np.mean(agree_sub)), 4),
             "fifo_topk_agreement": round(float(np.mean(agree_fifo)), 4),
+            "random_topk_agreement": round(float(np.mean(agree_rand)), 4),
+            "random_expected_agreement": round(k / cfg.pool_blocks, 4),
             "full_over_attention": round(float(np.median(t_full)) / ms_attn, 4)}
 
 
@@ -331,13 +397,20 @@ def hr_branch(pf, torch, pfgen, dev, gen_ms, reps=20):
     return out
 
 
-def generation_step(pf, torch, cfg, reps=2):
+def generation_step(pf, torch, cfg, reps=2, cadence=False):
     """One full generation step at the 2-minute pool shapes: every layer keeps
     its own resident cache (sink, a 117-slot pool holding 116 blocks, recent,
     current) and for each of the denoising steps runs select-and-place, the
     RoPE shift and the attention; after the steps every layer's new compressed
     block rolls into slot 116 in one batched call. Queries are drawn once per
-    layer (the kernels do not depend on their values' provenance)."""
+    layer (the kernels do not depend on their values' provenance).
+
+    cadence=True follows the pages instead of rerunning selection every step:
+    each layer selects once, at the block's first denoising step, with the
+    faster sub-sampled scoring (every 4th query row, every other head), places
+    and shifts; the later steps reuse the ids and the shifted keys (their
+    placement would give delta 0). The selection's share of the step is
+    reported against the pages' figure of under 1%."""
     L, S = cfg.layers, cfg.steps
     H, n, n_c, M, k, Bf = cfg.heads, cfg.n, cfg.n_c, cfg.pool_blocks, cfg.top_k, cfg.block_frames
     g = torch.Generator(device="cuda")
@@ -358,7 +431,9 @@ def generation_step(pf, torch, cfg, reps=2):
         layers.append(c)
     blk = torch.stack([draw(n_c) for _ in range(2 * L)]).view(2, L, n_c, H, 128)
     pool_k_all = [c["pool_k"] for c in layers]
-    ws = torch.empty(pf.pf_score_select_workspace_bytes(n, H, M, n_c), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(pf.pf_score_select_workspace_bytes(n, H, M, n_c),
+                         pf.pf_score_select_sub_workspace_bytes(n, H, 4, 2, M, n_c)), dtype=torch.uint8,
+                     device="cuda")
     o = torch.empty((n, H, 128), dtype=torch.bfloat16, device="cuda")
     aws = torch.empty(max(pf.pf_partition_attn_workspace_bytes(n, H, cfg.n_keys), 1), dtype=torch.uint8,
                       device="cuda")
@@ -366,14 +441,23 @@ def generation_step(pf, torch, cfg, reps=2):
     main = torch.cuda.current_stream()
     fr = (cfg.sink_blocks + M) * Bf
 
+    def select(c, pk):
+        if cadence:
+            pf.pf_score_select_sub(c["q"], pk, n_c, k, 4, 2, ids_out=c["ids"], scores_out=c["scores"],
+                                   workspace=ws)
+            pf.pf_selection_deltas(c["ids"], c["tags"], fr, Bf, deltas_out=c["deltas"])
+        else:
+            pf.pf_select_place(c["q"], pk, n_c, k, c["tags"], fr, Bf, ids_out=c["ids"], deltas_out=c["deltas"],
+                               scores_out=c["scores"], workspace=ws)
+
     def one_step():
-        for _ in range(S):
+        for s_i in range(S):
             for c in layers:
                 pk = c["pool_k"][:M * n_c]
                 pv = c["pool_v"][:M * n_c]
-                pf.pf_select_place(c["q"], pk, n_c, k, c["tags"], fr, Bf, ids_out=c["ids"], deltas_out=c["deltas"],
-                                   scores_out=c["scores"], workspace=ws)
-                pf.pf_rope_shift(pk, n_c, c["deltas"], c["ids"])
+                if s_i == 0 or not cadence:
+                    select(c, pk)
+                    pf.pf_rope_shift(pk, n_c, c["deltas"], c["ids"])
                 pf.pf_partition_attn(c["q"], c["sink_k"], c["sink_v"], pk, pv, n_c, c["ids"], c["recent_k"],
                                      c["recent_v"], c["cur_k"], c["cur_v"], o=o, workspace=aws)
         # every layer's new compressed block into pool slot M, on a second stream
@@ -391,12 +475,90 @@ def generation_step(pf, torch, cfg, reps=2):
     e1.record(main)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    # the selection calls of one generation step alone (every layer, as often
+    # as the step runs them), for their share of the step
+    n_sel = L * (1 if cadence else S)
+    e0.record(main)
+    for i in range(n_sel):
+        c = layers[i % L]
+        select(c, c["pool_k"][:M * n_c])
+    e1.record(main)
+    torch.cuda.synchronize()
+    sel_ms = e0.elapsed_time(e1)
     flops = L * S * attn_flops(n, cfg.n_keys, H)
     del layers, blk, pool_k_all
+    mode = ("the pages' cadence: sub-sampled selection (every 4th query row, every other head), placement and "
+            "shift at the first denoising step only" if cadence else
+            "selection, placement and shift rerun at every denoising step")
     return {"workload": f"{L} layers x {S} denoising steps at the {M}-block pool shapes ({cfg.n_keys} keys per "
-                        f"layer-step), then {L} roll-ins on a second stream",
+                        f"layer-step), then {L} roll-ins on a second stream; {mode}",
             "ms": round(ms, 3), "layer_steps": L * S, "ms_per_layer_step": round(ms / (L * S), 4),
-            "attention_tflops_over_the_step": round(flops / (ms * 1e-3) / 1e12, 1)}
+            "attention_tflops_over_the_step": round(flops / (ms * 1e-3) / 1e12, 1),
+            "selection_calls": n_sel, "selection_ms": round(sel_ms, 3),
+            "selection_frac_of_step": round(sel_ms / ms, 5)}
+
+
+def unbounded_c4(pf, torch, cfg, cpu=True, reps=3):
+    """The pages' unbounded contrast: one layer's 6,240 queries over all 748,800
+    full-resolution keys of a 2-minute video (sink + 117 recent blocks + the
+    current block, no compression or selection), drawn on the device from a
+    seed. Attention time and roofline; next to it the oracle's rate on a
+    bounded sample (one head, 128 queries over all keys, one core), scaled
+    linearly to the whole call and labelled as an extrapolation."""
+    H, n = cfg.heads, cfg.n
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+
+    def draw(rows):
+        return (torch.randn((rows, H, 128), generator=g, device="cuda") * cfg.scale).to(torch.bfloat16)
+
+    q = draw(n)
+    sink_k, sink_v = draw(cfg.n_sink), draw(cfg.n_sink)
+    rec_k, rec_v = draw(cfg.n_recent), draw(cfg.n_recent)
+    cur_k, cur_v = draw(n), draw(n)
+    n_keys = cfg.n_sink + cfg.n_recent + n
+    o = torch.empty_like(q)
+    ws = torch.empty(max(pf.pf_partition_attn_workspace_bytes(n, H, n_keys), 1), dtype=torch.uint8, device="cuda")
+    call = lambda: pf.pf_partition_attn(q, sink_k, sink_v, None, None, 1, None, rec_k, rec_v, cur_k, cur_v,
+                                        o=o, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    flops = attn_flops(n, n_keys, H)
+    med = float(np.median(ms))
+    out = {"workload": f"one layer, {n} queries x {H} heads over {n_keys} full-resolution keys "
+                       f"({cfg.n_sink} sink + {cfg.n_recent} recent + {n} current), no selection",
+           "flops_per_launch": flops, "ms": stats(ms),
+           "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+           "frac_mfma_peak": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "kv_bytes": int(2 * n_keys * H * 128 * 2)}
+    del q, sink_k, sink_v, rec_k, rec_v, cur_k, cur_v, o, ws
+    torch.cuda.empty_cache()
+    if cpu:
+        import oracle as O
+        rng = np.random.default_rng(cfg.seed)
+
+        def bits(rows):
+            return O.f64_to_bf16(rng.standard_normal((rows, 1, 128)).astype(np.float32) * cfg.scale)
+        rows = 128
+        qs, ks, vs = bits(rows), bits(n_keys), bits(n_keys)
+        t0 = time.perf_counter()
+        O.attn_partitioned(qs, [ks], [vs])
+        dt = time.perf_counter() - t0
+        rate = attn_flops(rows, n_keys, 1) / dt
+        out["cpu_oracle_extrapolated"] = {
+            "kind": "oracle, extrapolated", "sample": f"one head, {rows} queries over all {n_keys} keys, fp64 "
+                                                      f"numpy oracle, one core ({dt:.1f} s)",
+            "sample_tflops": round(rate / 1e12, 5),
+            "whole_call_s_one_core": round(flops / rate, 1),
+            "whole_call_s_16_cores_linear": round(flops / rate / 16, 1)}
+    return out
 
 
 def copy_calibration():
@@ -474,24 +636,28 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # K steps with an event after each call, for the per-call breakdown and the
+    # spread of step times (the clock takes about a dozen attention launches to
+    # settle, so these also run before the headline steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    part = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])   # [steps, 3] ms
+    ms_select, ms_rope, ms_attn = part.mean(axis=0)
+    step_each = np.array([e[0].elapsed_time(e[3]) for e in evs])
+
     # the timed steps, with nothing between the launches
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(args.warmup + args.steps + i)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    # the same number of steps again, with an event after each call, for the breakdown
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i, evs[i])
-    torch.cuda.synchronize()
-    part = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])   # [steps, 3] ms
-    ms_select, ms_rope, ms_attn = part.mean(axis=0)
     flops = attn_flops(cfg.n, cfg.n_keys, cfg.heads)
     value = flops / (ms_step * 1e-3) / 1e12
     attn_tflops = flops / (ms_attn * 1e-3) / 1e12
@@ -531,7 +697,13 @@ def main():
         "select_place_gbs": round(sel_bytes / (ms_select * 1e-3) / 1e9, 1),
         "rope_shift_gbs": round(rope_bytes / (ms_rope * 1e-3) / 1e9, 1),
         "input_gen_s": round(t_gen, 2),
+        "step_ms_stats": stats(step_each),
+        "attn_ms_stats": stats(part[:, 2]),
+        "attn_tflops_at_median": round(flops / (float(np.median(part[:, 2])) * 1e-3) / 1e12, 2),
     }
+    if args.layer_step_only:
+        print(json.dumps(out), flush=True)
+        return
     out["selection_cadence"] = selection_cadence(pf, torch, pfgen, dev, ms_attn)
     out["rollin_overlap"] = rollin_overlap(pf, torch, pfgen, step_attn=lambda: pf.pf_partition_attn(
         t["q"], t["sink_k"], t["sink_v"], t["pool_k"], t["pool_v"], cfg.n_c, ids, t["recent_k"], t["recent_v"],
@@ -539,6 +711,9 @@ def main():
     out["hr_branch"] = hr_branch(pf, torch, pfgen, dev, gen_ms=pfgen.C3.layers * pfgen.C3.steps * ms_step)
     if not args.no_batched:
         out["generation_step"] = generation_step(pf, torch, pfgen.C3)
+        out["generation_step_pages_cadence"] = generation_step(pf, torch, pfgen.C3, cadence=True)
+    if not args.no_c4:
+        out["unbounded_c4"] = unbounded_c4(pf, torch, pfgen.C4, cpu=not args.no_cpu)
     if not args.no_batched:
         hb = hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, 5)
         # one generation step = layers x denoising steps layer-steps; the eviction

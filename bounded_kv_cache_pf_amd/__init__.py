@@ -49,6 +49,7 @@ _SIGNATURES = {
                          _sz, _p], _i32),
     "pf_select_place_batched": ([_p, _i64, _i64, _i32, _p, _i64, _i32, _i32, _i32, _p, ctypes.c_int32,
                                  ctypes.c_int32, _i32, _p, _p, _p, _p, _sz, _p], _i32),
+    "pf_select_random": ([_i32, _i32, ctypes.c_uint64, ctypes.c_uint64, _i32, _p, _p], _i32),
     "pf_hr_conv_workspace_bytes": ([_i32] * 9, _sz),
     "pf_hr_conv": ([_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32, _i32, _p, _p, _sz, _p], _i32),
     "pf_hr_branch_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _p, _i32], _sz),
@@ -260,6 +261,20 @@ def pf_score_select_sub(q, pool_k, n_c: int, top_k: int, q_step: int, head_step:
                                    _ptr(ids_out), _ptr(scores_out), _ptr(ws), have, _stream(stream)),
            "pf_score_select_sub")
     return ids_out, scores_out
+
+
+def pf_select_random(n_blocks: int, top_k: int, seed: int, counter: int, n_batch: int = 1, ids_out=None,
+                     device="cuda", stream=None):
+    """The random-selection baseline: top_k distinct blocks of n_blocks per cache,
+    ascending, from stream (seed, counter + b). Returns int32 [n_batch][top_k]
+    (or [top_k] when n_batch == 1 and ids_out is None)."""
+    torch = _torch()
+    dev = torch.device(device) if ids_out is None else ids_out.device
+    shape = (n_batch, top_k) if n_batch > 1 else top_k
+    ids_out = _out_i32(ids_out, shape, dev, stream, "ids_out")
+    _check(lib.pf_select_random(n_blocks, top_k, seed & (2 ** 64 - 1), counter & (2 ** 64 - 1), n_batch,
+                                _ptr(ids_out), _stream(stream)), "pf_select_random")
+    return ids_out
 
 
 def pf_selection_deltas(ids, pos_tags, recent_first_frame: int, block_frames: int, deltas_out=None,

@@ -317,6 +317,50 @@ __global__ __launch_bounds__(PF_MAX_TOPK) void deltas_kernel(const int32_t* __re
             deltas + b * top_k + r);
 }
 
+// Random-selection baseline [digest, 实验结果; arXiv HTML, "FIFO vs. Dynamic
+// Context Selection"]: k distinct blocks by Floyd's sampling algorithm
+// (Bentley and Floyd, CACM 1987) over a counter-based SplitMix64 stream
+// (Steele, Lea and Flood, OOPSLA 2014). Draw i (1, 2, ...) of stream
+// (seed, counter) is mix(seed + (counter * 2^32 + i) * gamma).
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t splitmix_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// One workgroup per cache b (stream counter + b). Thread 0 runs Floyd's steps
+// with a membership bitmap in LDS; then thread r writes kept value r at its
+// rank, so the ids come out ascending.
+__global__ __launch_bounds__(PF_MAX_TOPK) void random_select_kernel(int n_blocks, int top_k, uint64_t seed,
+                                                                     uint64_t counter, int32_t* __restrict__ ids_out) {
+  __shared__ uint32_t member[PF_MAX_BLOCKS / 32];
+  __shared__ int32_t kept[PF_MAX_TOPK];
+  const int tid = static_cast<int>(threadIdx.x);
+  const uint64_t c = counter + blockIdx.x;
+  for (int i = tid; i < PF_MAX_BLOCKS / 32; i += blockDim.x) member[i] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    for (int r = 0; r < top_k; ++r) {
+      const uint32_t j = static_cast<uint32_t>(n_blocks - top_k + r);
+      const uint64_t x = splitmix_mix(seed + ((c << 32) + static_cast<uint64_t>(r + 1)) * kGamma);
+      const uint32_t t = static_cast<uint32_t>(((x >> 32) * (static_cast<uint64_t>(j) + 1)) >> 32);
+      const bool seen = (member[t >> 5] >> (t & 31)) & 1u;
+      const uint32_t v = seen ? j : t;
+      member[v >> 5] |= 1u << (v & 31);
+      kept[r] = static_cast<int32_t>(v);
+    }
+  }
+  __syncthreads();
+  if (tid < top_k) {
+    const int32_t me = kept[tid];
+    int rank = 0;
+    for (int r = 0; r < top_k; ++r) rank += kept[r] < me;
+    ids_out[static_cast<int64_t>(blockIdx.x) * top_k + rank] = me;
+  }
+}
+
 bool valid_sizes(int64_t n_q, int n_heads, int n_blocks, int n_c, int n_batch) {
   return n_q >= 1 && n_heads >= 1 && n_heads <= PF_MAX_HEADS && n_blocks >= 1 && n_blocks <= PF_MAX_BLOCKS &&
          n_c >= 1 && n_batch >= 1 && n_batch <= PF_MAX_BATCH;
@@ -493,4 +537,19 @@ extern "C" pf_status pf_selection_deltas(const int32_t* ids, int top_k, int32_t*
                                          void* stream) {
   return pf_selection_deltas_batched(ids, top_k, pos_tags, n_blocks, recent_first_frame, block_frames, 1,
                                      deltas_out, stream);
+}
+
+extern "C" pf_status pf_select_random(int n_blocks, int top_k, uint64_t seed, uint64_t counter, int n_batch,
+                                      int32_t* ids_out, void* stream) {
+  PF_REQUIRE_PTR(ids_out);
+  PF_REQUIRE(n_blocks >= 1 && n_blocks <= PF_MAX_BLOCKS, PF_ERR_UNSUPPORTED,
+             "n_blocks must be in [1, %d] (got %d)", PF_MAX_BLOCKS, n_blocks);
+  PF_REQUIRE(top_k >= 1 && top_k <= n_blocks && top_k <= PF_MAX_TOPK, PF_ERR_RANGE,
+             "top_k must be in [1, min(n_blocks, %d)] (got %d)", PF_MAX_TOPK, top_k);
+  PF_REQUIRE(n_batch >= 1 && n_batch <= PF_MAX_BATCH, PF_ERR_RANGE, "n_batch must be in [1, %d] (got %d)",
+             PF_MAX_BATCH, n_batch);
+  PF_REQUIRE((reinterpret_cast<uintptr_t>(ids_out) & 3u) == 0, PF_ERR_MISALIGNED, "ids_out is not 4-byte aligned");
+  hipLaunchKernelGGL(random_select_kernel, dim3(n_batch), dim3(PF_MAX_TOPK), 0, static_cast<hipStream_t>(stream),
+                     n_blocks, top_k, seed, counter, ids_out);
+  return pf::launch_status("pf_select_random");
 }

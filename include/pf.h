@@ -134,6 +134,23 @@ pf_status pf_score_select_batched(const pf_bf16* q, int64_t q_batch_stride, int6
                                   int top_k, int n_batch, int32_t* ids_out, float* scores_out,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Random selection, the pages' weakest baseline against dynamic selection
+ * [digest, 实验结果 (dynamic vs FIFO vs random); arXiv HTML, "FIFO vs. Dynamic
+ * Context Selection"]. The pages name no generator; this library draws k
+ * distinct blocks with Floyd's sampling algorithm (Bentley and Floyd, CACM
+ * 1987): step r (r = 0..top_k-1) takes j = n_blocks - top_k + r and
+ * t = floor(hi32(x_{r+1}) * (j + 1) / 2^32), keeping t unless it was kept
+ * already, else j. x_i is draw i of a counter-based SplitMix64 stream
+ * (Steele, Lea and Flood, OOPSLA 2014):
+ *   x_i = mix(seed + (c * 2^32 + i) * 0x9E3779B97F4A7C15)   (mod 2^64)
+ * with c = counter + b for cache b of the batch. ids_out[b*top_k ..] gets the
+ * ids in ascending order. The FIFO baseline needs no kernel: it keeps blocks
+ * n_blocks - top_k .. n_blocks - 1.
+ * Limits: 1 <= n_blocks <= PF_MAX_BLOCKS, 1 <= top_k <= min(n_blocks,
+ * PF_MAX_TOPK), 1 <= n_batch <= PF_MAX_BATCH. */
+pf_status pf_select_random(int n_blocks, int top_k, uint64_t seed, uint64_t counter, int n_batch,
+                           int32_t* ids_out, void* stream);
+
 /* ------------------------------------------------------------------------- *
  * Placement of the selected blocks -> per-block temporal shift delta
  * [PackForcing arXiv HTML, "The Position Misalignment Problem" and

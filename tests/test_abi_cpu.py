@@ -68,6 +68,16 @@ def test_score_select_validation(pf):
     assert _err(pf, L.pf_score_select(A, 0, 12, B, 40, 182, 16, C, None, A, ws, None))[0] == "PF_ERR_SHAPE"
 
 
+def test_random_select_validation(pf):
+    L = pf.lib
+    assert _err(pf, L.pf_select_random(40, 16, 1, 0, 1, None, None))[0] == "PF_ERR_NULL"
+    assert _err(pf, L.pf_select_random(40, 41, 1, 0, 1, A, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_select_random(40, 0, 1, 0, 1, A, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_select_random(5000, 16, 1, 0, 1, A, None))[0] == "PF_ERR_UNSUPPORTED"
+    assert _err(pf, L.pf_select_random(40, 16, 1, 0, 0, A, None))[0] == "PF_ERR_RANGE"
+    assert _err(pf, L.pf_select_random(40, 16, 1, 0, 1, A + 2, None))[0] == "PF_ERR_MISALIGNED"
+
+
 def test_deltas_validation(pf):
     L = pf.lib
     assert _err(pf, L.pf_selection_deltas(None, 16, B, 40, 168, 4, C, None))[0] == "PF_ERR_NULL"

@@ -214,3 +214,17 @@ def test_select_place_batched_equals_single_calls():
         assert d[b].cpu().numpy().tolist() == d1.cpu().numpy().tolist()
         assert np.array_equal(s[b].cpu().numpy().view(np.uint32), s1.cpu().numpy().view(np.uint32))
         assert tags[b].cpu().numpy().tolist() == t1.cpu().numpy().tolist()
+
+
+def test_random_selector_matches_oracle_bit_exact():
+    # the random-selection baseline: the same counter-based stream and Floyd
+    # steps on both sides, so the ids agree exactly for every stream
+    say("test_random_selector_matches_oracle_bit_exact")
+    for n_blocks, k, seed in ((40, 16, 1234), (116, 16, 99), (10, 4, 0), (16, 16, 5), (4096, 256, 2 ** 63 + 17),
+                              (1, 1, 3)):
+        nb = 7
+        got = pf.pf_select_random(n_blocks, k, seed, 1000, n_batch=nb).cpu().numpy()
+        for b in range(nb):
+            assert got[b].tolist() == O.select_random(n_blocks, k, seed, 1000 + b), (n_blocks, k, seed, b)
+    one = pf.pf_select_random(40, 16, 1234, 1000).cpu().numpy().tolist()
+    assert one == O.select_random(40, 16, 1234, 1000)
