@@ -62,6 +62,12 @@ _SIGNATURES = {
                            _p, _p, _i64,
                            _p, _p, _i64,
                            ctypes.c_float, _p, _p, _p, _sz, _p], _i32),
+    "pf_partition_attn_noalloc": ([_p, _i64, _i32,
+                                   _p, _p, _i64,
+                                   _p, _p, _i32, _i32, _p, _i32,
+                                   _p, _p, _i64,
+                                   _p, _p, _i64,
+                                   ctypes.c_float, _p, _p, _p], _i32),
 }
 for _name, (_args, _ret) in _SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -525,6 +531,27 @@ def pf_partition_attn(q, sink_k, sink_v, pool_k, pool_v, n_c: int, mid_ids, rece
                                  _ptr(cur_k), _ptr(cur_v), n_cur,
                                  float(scale), _ptr(o), _ptr(lse), _ptr(ws), have, _stream(stream)),
            "pf_partition_attn")
+    return o, lse
+
+
+def pf_partition_attn_noalloc(q, sink_k, sink_v, pool_k, pool_v, n_c: int, mid_ids, recent_k, recent_v, cur_k,
+                              cur_v, o, lse=None, scale: float = 0.0, stream=None):
+    """pf_partition_attn with the library's fixed device scratch array in place of a
+    workspace: the caller passes every buffer, including o (and lse if wanted),
+    and the call allocates nothing. Calls overlapping on one GPU race."""
+    heads, n_q, n_sink, n_sel, n_blocks, n_rec, n_cur = _attn_shapes(
+        q, sink_k, sink_v, pool_k, pool_v, n_c, mid_ids, recent_k, recent_v, cur_k, cur_v)
+    if o is None:
+        raise TypeError("o is required: pf_partition_attn_noalloc allocates nothing")
+    o, lse = _attn_out(o, lse, False, q, heads, n_q, None)
+    _check(lib.pf_partition_attn_noalloc(_ptr(q), n_q, heads,
+                                         _ptr(sink_k), _ptr(sink_v), n_sink,
+                                         _ptr(pool_k) if n_sel else None, _ptr(pool_v) if n_sel else None,
+                                         n_blocks, n_c, _ptr(mid_ids) if n_sel else None, n_sel,
+                                         _ptr(recent_k), _ptr(recent_v), n_rec,
+                                         _ptr(cur_k), _ptr(cur_v), n_cur,
+                                         float(scale), _ptr(o), _ptr(lse), _stream(stream)),
+           "pf_partition_attn_noalloc")
     return o, lse
 
 

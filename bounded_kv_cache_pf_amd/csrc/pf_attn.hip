@@ -732,13 +732,43 @@ extern "C" size_t pf_partition_attn_workspace_bytes(int64_t n_q, int n_heads, in
   return make_plan(n_q, n_heads, n_keys, resident_workgroups()).ws_bytes;
 }
 
-extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* sink_k,
-                                       const pf_bf16* sink_v, int64_t n_sink, const pf_bf16* pool_k,
-                                       const pf_bf16* pool_v, int n_blocks, int n_c, const int32_t* mid_ids,
-                                       int n_sel, const pf_bf16* recent_k, const pf_bf16* recent_v,
-                                       int64_t n_recent, const pf_bf16* cur_k, const pf_bf16* cur_v, int64_t n_cur,
-                                       float scale, pf_bf16* o, float* lse, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+namespace {
+
+// The partial results of split units live in the caller's workspace, or, for
+// pf_partition_attn_noalloc, in this fixed device array (one per GPU, for the
+// life of the process). Host code never names the array in a launch: it
+// passes the device address that hipGetSymbolAddress returns for the current
+// device.
+constexpr size_t kScratchBytes = size_t{40} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+pf_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return pf::fail(PF_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return pf::fail(PF_ERR_UNSUPPORTED, "device %d is beyond the 64 this library tracks", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess || p == nullptr)
+      return pf::fail(PF_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(g));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return PF_OK;
+}
+
+// Validation and launch shared by both entry points. With `use_scratch`, the
+// partials go to the device's scratch array instead of `workspace`.
+pf_status attn_call(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* sink_k, const pf_bf16* sink_v,
+                    int64_t n_sink, const pf_bf16* pool_k, const pf_bf16* pool_v, int n_blocks, int n_c,
+                    const int32_t* mid_ids, int n_sel, const pf_bf16* recent_k, const pf_bf16* recent_v,
+                    int64_t n_recent, const pf_bf16* cur_k, const pf_bf16* cur_v, int64_t n_cur, float scale,
+                    pf_bf16* o, float* lse, void* workspace, size_t workspace_bytes, bool use_scratch,
+                    void* stream) {
   PF_REQUIRE_PTR(q);
   PF_REQUIRE_PTR(o);
   PF_REQUIRE_ALIGNED(q);
@@ -792,7 +822,15 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
   PF_REQUIRE(num_qtiles * n_heads < 0x7FFFFFFF, PF_ERR_UNSUPPORTED, "too many query tiles");
 
   const Plan p = make_plan(n_q, n_heads, n_keys, resident_workgroups());
-  if (p.ws_bytes > 0) {
+  if (use_scratch) {
+    PF_REQUIRE(p.ws_bytes <= kScratchBytes, PF_ERR_UNSUPPORTED,
+               "this shape needs %zu bytes of partials, beyond the %zu-byte scratch array", p.ws_bytes,
+               kScratchBytes);
+    if (p.ws_bytes > 0) {
+      const pf_status s = scratch_address(&workspace);
+      if (s != PF_OK) return s;
+    }
+  } else if (p.ws_bytes > 0) {
     PF_REQUIRE(workspace != nullptr, PF_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", p.ws_bytes);
     PF_REQUIRE(workspace_bytes >= p.ws_bytes, PF_ERR_WORKSPACE, "workspace has %zu bytes, need %zu",
                workspace_bytes, p.ws_bytes);
@@ -850,4 +888,28 @@ extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_head
   if (s != PF_OK || p.n_seg <= 1) return s;
   hipLaunchKernelGGL(merge_kernel, dim3(p.n_tail, kBM / kMergeQueries), dim3(256), 0, st, a);
   return pf::launch_status("pf_partition_attn (merge)");
+}
+
+}  // namespace
+
+extern "C" pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* sink_k,
+                                       const pf_bf16* sink_v, int64_t n_sink, const pf_bf16* pool_k,
+                                       const pf_bf16* pool_v, int n_blocks, int n_c, const int32_t* mid_ids,
+                                       int n_sel, const pf_bf16* recent_k, const pf_bf16* recent_v,
+                                       int64_t n_recent, const pf_bf16* cur_k, const pf_bf16* cur_v, int64_t n_cur,
+                                       float scale, pf_bf16* o, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return attn_call(q, n_q, n_heads, sink_k, sink_v, n_sink, pool_k, pool_v, n_blocks, n_c, mid_ids, n_sel, recent_k,
+                   recent_v, n_recent, cur_k, cur_v, n_cur, scale, o, lse, workspace, workspace_bytes, false, stream);
+}
+
+extern "C" pf_status pf_partition_attn_noalloc(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* sink_k,
+                                               const pf_bf16* sink_v, int64_t n_sink, const pf_bf16* pool_k,
+                                               const pf_bf16* pool_v, int n_blocks, int n_c,
+                                               const int32_t* mid_ids, int n_sel, const pf_bf16* recent_k,
+                                               const pf_bf16* recent_v, int64_t n_recent, const pf_bf16* cur_k,
+                                               const pf_bf16* cur_v, int64_t n_cur, float scale, pf_bf16* o,
+                                               float* lse, void* stream) {
+  return attn_call(q, n_q, n_heads, sink_k, sink_v, n_sink, pool_k, pool_v, n_blocks, n_c, mid_ids, n_sel, recent_k,
+                   recent_v, n_recent, cur_k, cur_v, n_cur, scale, o, lse, nullptr, 0, true, stream);
 }

@@ -289,6 +289,28 @@ pf_status pf_partition_attn(const pf_bf16* q, int64_t n_q, int n_heads,
                             float scale, pf_bf16* o, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* pf_partition_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results as pf_partition_attn, with no
+ * workspace argument. The partial results that a workspace would hold go to a
+ * fixed 40 MiB device array inside the library, one per GPU, kept until the
+ * process ends; the call itself allocates nothing. Its device address is
+ * looked up once per device, on the first call with that device current.
+ * Shapes whose partials exceed the array (the size
+ * pf_partition_attn_workspace_bytes reports, at most 34 MB on a 256-CU
+ * MI355X) return PF_ERR_UNSUPPORTED before anything is enqueued. The array is
+ * shared by every call on a GPU and keeps the last call's contents (no call
+ * reads a partial it did not write first): calls that overlap on one GPU,
+ * on any streams, race and must be ordered by the caller. Other arguments,
+ * limits and errors as pf_partition_attn. */
+pf_status pf_partition_attn_noalloc(const pf_bf16* q, int64_t n_q, int n_heads,
+                                    const pf_bf16* sink_k, const pf_bf16* sink_v, int64_t n_sink,
+                                    const pf_bf16* pool_k, const pf_bf16* pool_v, int n_blocks, int n_c,
+                                    const int32_t* mid_ids, int n_sel,
+                                    const pf_bf16* recent_k, const pf_bf16* recent_v, int64_t n_recent,
+                                    const pf_bf16* cur_k, const pf_bf16* cur_v, int64_t n_cur,
+                                    float scale, pf_bf16* o, float* lse, void* stream);
+
 /* ------------------------------------------------------------------------- *
  * Roll-in of a compressed block into the mid pool
  * [PackForcing arXiv HTML, "Dual-Resolution Shifting Mechanism": when a block
