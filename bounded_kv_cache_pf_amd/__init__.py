@@ -252,6 +252,11 @@ def pf_select_place(q, pool_k, n_c: int, top_k: int, pos_tags, recent_first_fram
     return ids_out, deltas_out, scores_out
 
 
+def pf_score_select_sub_workspace_bytes(n_q: int, n_heads: int, q_step: int, head_step: int, n_blocks: int,
+                                        n_c: int) -> int:
+    return int(lib.pf_score_select_sub_workspace_bytes(n_q, n_heads, q_step, head_step, n_blocks, n_c))
+
+
 def pf_score_select_sub(q, pool_k, n_c: int, top_k: int, q_step: int, head_step: int, ids_out=None,
                         scores_out=None, workspace=None, stream=None) -> Tuple[object, object]:
     """Top-k scored from query rows 0, q_step, ... and heads 0, head_step, ... only."""
@@ -261,7 +266,7 @@ def pf_score_select_sub(q, pool_k, n_c: int, top_k: int, q_step: int, head_step:
     _check_inputs(q.device, pool_k=pool_k)
     ids_out = _out_i32(ids_out, top_k, q.device, stream, "ids_out")
     scores_out = _out_f32(scores_out, n_blocks, q.device, stream, "scores_out")
-    need = int(lib.pf_score_select_sub_workspace_bytes(n_q, heads, q_step, head_step, n_blocks, n_c))
+    need = pf_score_select_sub_workspace_bytes(n_q, heads, q_step, head_step, n_blocks, n_c)
     ws, have = _workspace(workspace, need, q.device, stream)
     _check(lib.pf_score_select_sub(_ptr(q), n_q, heads, q_step, head_step, _ptr(pool_k), n_blocks, n_c, top_k,
                                    _ptr(ids_out), _ptr(scores_out), _ptr(ws), have, _stream(stream)),

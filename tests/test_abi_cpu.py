@@ -344,3 +344,11 @@ def test_binding_checks_selection_outputs(pf):
         pf.pf_score_select_batched(qb, pb, n_c, k, ids_out=_fake((3, k - 1), torch.int32))
     with pytest.raises(ValueError, match="deltas_out"):
         pf.pf_selection_deltas(_fake((k,), torch.int32), tags, 48, 4, deltas_out=_fake((k - 1,), torch.int32))
+
+
+def test_bench_calls_only_bound_functions(pf):
+    # every binding function bench.py calls exists (a missing one fails the
+    # GPU run only after minutes of work)
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    for name in sorted(set(re.findall(r"pf\.(pf_[a-z_0-9]+)", src))):
+        assert hasattr(pf, name), name
