@@ -15,7 +15,9 @@ import os
 from typing import Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpf.so")
+# PF_LIBRARY may name another build of the same library (the host-sanitizer
+# build, libpf_asan.so, for the sanitized host-side tests)
+LIB_PATH = os.environ.get("PF_LIBRARY") or os.path.join(_HERE, "libpf.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bounded_kv_cache_pf_amd.build` "

@@ -1,4 +1,10 @@
-"""Compile libpf.so (HIP for gfx950) in place, next to this file."""
+"""Compile libpf.so (HIP for gfx950) in place, next to this file.
+
+`python -m bounded_kv_cache_pf_amd.build --sanitize` builds libpf_asan.so
+instead: the same sources with AddressSanitizer and UndefinedBehaviorSanitizer
+on the host code only (argument validation, planning, error reporting); the
+device code is compiled as usual. It is for running the host-side tests under
+the sanitizers; nothing loads it by default."""
 from __future__ import annotations
 
 import os
@@ -10,6 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpf.so")
+ASAN_LIB = os.path.join(HERE, "libpf_asan.so")
 SOURCES = ["pf_status.hip", "pf_rope.hip", "pf_select.hip", "pf_attn.hip", "pf_rollin.hip", "pf_hr.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -22,18 +29,36 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# host-side sanitizers: each -fsanitize= applies to the host compilation only
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (preloaded into the
+    process that loads libpf_asan.so), or '' if it is not installed."""
+    res = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        found = glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        path = found[0] if found else ""
+    return path
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+    out = ASAN_LIB if sanitize else LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(SANITIZE_FLAGS if sanitize else []), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

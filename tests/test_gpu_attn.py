@@ -62,6 +62,17 @@ def test_attn_full_size_sampled_rows(cfg):
     _compare(c, cfg.n_c, ids, rows=_sample_rows(cfg.n), label=cfg.name)
 
 
+def test_attn_default_layer_all_rows():
+    # every one of the 6,240 x 12 query rows of the default layer against the
+    # oracle (about 20 s of fp64 on the host), so full-size parity does not
+    # rest on sampled rows alone
+    say("test_attn_default_layer_all_rows")
+    cfg = pfgen.C1
+    c = pfgen.make(cfg)
+    ids = sorted(np.random.default_rng(cfg.seed + 3).choice(cfg.pool_blocks, cfg.top_k, replace=False).tolist())
+    _compare(c, cfg.n_c, ids, label="C1 all rows")
+
+
 def test_attn_sharp_scores():
     # Q x 8: score std ~4, a peaked softmax that exercises the running-max rescale
     say("test_attn_sharp_scores")
