@@ -75,17 +75,29 @@ def kernel_source_sha(text=None):
     return hashlib.sha256("\n".join(c for c in code if c).encode()).hexdigest()[:16]
 
 
-def traffic_from_counters():
-    """HBM bytes per attention launch from the committed counter summary, if it
-    was taken on the current kernel source."""
+def counters_for_current_source():
+    """The committed counter summary of the attention kernel, if it was taken
+    on the current kernel source (else None)."""
     try:
         with open(PMC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_sha") != kernel_source_sha():
-        return None
-    return d.get("hbm_bytes_per_launch")
+    return d if d.get("source_sha") == kernel_source_sha() else None
+
+
+def traffic_from_counters():
+    """HBM bytes per attention launch from the committed counter summary."""
+    d = counters_for_current_source()
+    return None if d is None else d.get("hbm_bytes_per_launch")
+
+
+def mfma_busy_from_counters():
+    """The attention kernel's MFMA busy fraction (busy cycles over all SIMD
+    cycles of the dispatch, at the clock it ran at) from the committed counters."""
+    d = counters_for_current_source()
+    m = None if d is None else d.get("mfma")
+    return None if m is None else round(m["mfma_busy_frac"], 4)
 
 
 def host_info():
@@ -688,6 +700,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_counters(),
+                     "mfma_busy_counter": mfma_busy_from_counters(),
                      "kernel": "partition_attn_kernel", "flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": attn_bytes},
         "kernels_ms": {"select_place": round(float(ms_select), 5), "rope_shift": round(float(ms_rope), 5),
