@@ -15,9 +15,9 @@
 //   2. qsum:   the Q partials are added per column, 16 interleaved runs of
 //              segments combined in a fixed order;
 //   3. score:  one workgroup per block adds its slices and dots with the Q sum;
-//   4. topk:   one workgroup per cache bitonic-sorts (score desc, index asc)
-//              keys in LDS, writes the first k ids in ascending order and,
-//              for the fused select-and-place call, places them.
+//   4. topk:   one workgroup per cache ranks (score desc, index asc) the keys
+//              in LDS, writes the first k ids in ascending order and, for the
+//              fused select-and-place call, places them.
 // Every sum runs in a fixed order that does not depend on the batch, so
 // identical blocks get identical scores, repeated calls give identical bits,
 // and a batched call gives the bits of the single calls.
@@ -36,8 +36,6 @@ constexpr int kTargetSegments = 256;   // pool slices aimed at per cache (at lea
 constexpr int kRowUnroll = 4;      // rows whose loads a colsum thread keeps in flight
 constexpr int kQsumCols = 64;      // columns per qsum workgroup
 constexpr int kQsumRuns = 16;      // interleaved runs of Q segments per column
-constexpr int kScoreThreads = 256;
-constexpr int kScoreColsPerThread = PF_MAX_HEADS * PF_HEAD_DIM / kScoreThreads;   // 16
 
 struct SelectPlan {
   int H, cw;          // heads, 16-byte column chunks per row (H*16)
@@ -210,63 +208,87 @@ __device__ __forceinline__ void place_one(int32_t id, int r, int top_k, int32_t*
   tags[id] = target;
 }
 
-// 3. Block score: one workgroup per pool block and cache. Thread t owns the
-// columns t + 256 i; each column's slices are added in slice order, then the
-// products with the Q sum in column order, then a fixed tree over threads.
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(float* __restrict__ ws, int64_t cache_floats,
-                                                              int64_t qsum_off, int64_t scores_off,
-                                                              float* __restrict__ scores_out, int n_blocks,
-                                                              int nq_seg, int ksub, int cols, float norm) {
-  __shared__ float red[kScoreThreads];
+// 3. Block score: one workgroup per pool block and cache, one thread per four
+// columns (cols / 4 threads, rounded up to whole waves). A thread adds its columns' slices in slice
+// order (every load issued before the first add), dots them with the Q sum
+// in column order, and the threads' products are added by a fixed tree:
+// within each wave by lane-distance halving, then the waves in order.
+__global__ __launch_bounds__(1024) void score_kernel(float* __restrict__ ws, int64_t cache_floats,
+                                                     int64_t qsum_off, int64_t scores_off,
+                                                     float* __restrict__ scores_out, int n_blocks, int nq_seg,
+                                                     int ksub, int cols, float norm) {
+  __shared__ float red[16];
   const int blk = blockIdx.x;
   const int t = threadIdx.x;
-  float* cache = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
-  const float* kp = cache + (static_cast<int64_t>(nq_seg) + static_cast<int64_t>(blk) * ksub) * cols;
-  float ks[kScoreColsPerThread];
-#pragma unroll
-  for (int i = 0; i < kScoreColsPerThread; ++i) ks[i] = 0.f;
-  for (int s = 0; s < ksub; ++s) {
-    const float* row = kp + static_cast<int64_t>(s) * cols;
-#pragma unroll
-    for (int i = 0; i < kScoreColsPerThread; ++i) {
-      const int c = t + kScoreThreads * i;
-      if (c < cols) ks[i] += row[c];
-    }
-  }
+  const float* cache = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
+  const float4* kp =
+      reinterpret_cast<const float4*>(cache + (static_cast<int64_t>(nq_seg) + static_cast<int64_t>(blk) * ksub) * cols) + t;
+  const int c4 = cols >> 2;
   float dot = 0.f;
+  if (t < c4) {
+    float4 ks = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = 0;
+    for (; s + 7 < ksub; s += 8) {
+      float4 v[8];
 #pragma unroll
-  for (int i = 0; i < kScoreColsPerThread; ++i) {
-    const int c = t + kScoreThreads * i;
-    if (c < cols) dot += cache[qsum_off + c] * ks[i];
+      for (int u = 0; u < 8; ++u) v[u] = kp[static_cast<int64_t>(s + u) * c4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ks.x += v[u].x; ks.y += v[u].y; ks.z += v[u].z; ks.w += v[u].w;
+      }
+    }
+    for (; s < ksub; ++s) {
+      const float4 v = kp[static_cast<int64_t>(s) * c4];
+      ks.x += v.x; ks.y += v.y; ks.z += v.z; ks.w += v.w;
+    }
+    const float4 qv = reinterpret_cast<const float4*>(cache + qsum_off)[t];
+    dot = qv.x * ks.x;
+    dot += qv.y * ks.y;
+    dot += qv.z * ks.z;
+    dot += qv.w * ks.w;
   }
-  red[t] = dot;
+  // every lane of the (whole) waves takes part; lanes past the columns add 0
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) dot += __shfl_xor(dot, d);
+  const int n_waves = (blockDim.x + 63) >> 6;
+  if ((t & 63) == 0) red[t >> 6] = dot;
   __syncthreads();
-  for (int w = kScoreThreads / 2; w > 0; w >>= 1) {
-    if (t < w) red[t] += red[t + w];
-    __syncthreads();
-  }
   if (t == 0) {
-    const float s = red[0] * norm;
-    cache[scores_off + blk] = s;
-    if (scores_out) scores_out[static_cast<int64_t>(blockIdx.y) * n_blocks + blk] = s;
+    float total = red[0];
+    for (int w = 1; w < n_waves; ++w) total += red[w];
+    const float sc = total * norm;
+    float* cw = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
+    cw[scores_off + blk] = sc;
+    if (scores_out) scores_out[static_cast<int64_t>(blockIdx.y) * n_blocks + blk] = sc;
   }
 }
 
-// 4. Top-k: bitonic sort of up to PF_MAX_BLOCKS keys in LDS, one workgroup per
-// cache; with tags != nullptr it also places the selected blocks.
+// 4. Top-k, one workgroup per cache: the k smallest rank keys, written in
+// ascending id order; with tags != nullptr it also places the selected blocks.
+// Up to one key per thread, a key's rank is the count of smaller keys (all
+// keys differ, the index breaks ties); more blocks than threads are sorted
+// (bitonic, in LDS).
 constexpr int kTopkThreads = 1024;
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ ws, int64_t cache_floats,
-                                                             int64_t scores_off, int n_blocks, int top_k,
-                                                             int32_t* __restrict__ ids_out,
-                                                             int32_t* __restrict__ tags, int32_t recent_first_frame,
-                                                             int32_t block_frames, int32_t* __restrict__ deltas) {
-  __shared__ uint64_t keys[PF_MAX_BLOCKS];
-  __shared__ uint32_t chosen[PF_MAX_TOPK];
-  __shared__ int32_t sorted_ids[PF_MAX_TOPK];
-  const int64_t b = blockIdx.x;
-  const float* scores = ws + b * cache_floats + scores_off;
-  int32_t* ids = ids_out + b * top_k;
+// chosen[r] = index of the key of rank r, r < top_k
+__device__ __forceinline__ void topk_by_rank(const float* scores, int n_blocks, int top_k, uint64_t* keys,
+                                             uint32_t* chosen) {
+  const int tid = static_cast<int>(threadIdx.x);
+  uint64_t mine = ~0ull;
+  if (tid < n_blocks) {
+    mine = rank_key(scores[tid], static_cast<uint32_t>(tid));
+    keys[tid] = mine;
+  }
+  __syncthreads();
+  if (tid < n_blocks) {
+    int rank = 0;
+    for (int j = 0; j < n_blocks; ++j) rank += keys[j] < mine;
+    if (rank < top_k) chosen[rank] = static_cast<uint32_t>(tid);
+  }
+}
+
+__device__ __forceinline__ void topk_by_sort(const float* scores, int n_blocks, int top_k, uint64_t* keys,
+                                             uint32_t* chosen) {
   int P = 1;
   while (P < n_blocks) P <<= 1;
   for (int i = threadIdx.x; i < P; i += blockDim.x)
@@ -290,7 +312,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
   const int tid = static_cast<int>(threadIdx.x);
   if (tid < top_k) chosen[tid] = static_cast<uint32_t>(keys[tid] & 0xFFFFFFFFu);
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ ws, int64_t cache_floats,
+                                                             int64_t scores_off, int n_blocks, int top_k,
+                                                             int32_t* __restrict__ ids_out,
+                                                             int32_t* __restrict__ tags, int32_t recent_first_frame,
+                                                             int32_t block_frames, int32_t* __restrict__ deltas) {
+  __shared__ uint64_t keys[PF_MAX_BLOCKS];
+  __shared__ uint32_t chosen[PF_MAX_TOPK];
+  __shared__ int32_t sorted_ids[PF_MAX_TOPK];
+  const int64_t b = blockIdx.x;
+  const float* scores = ws + b * cache_floats + scores_off;
+  int32_t* ids = ids_out + b * top_k;
+  if (n_blocks <= kTopkThreads)
+    topk_by_rank(scores, n_blocks, top_k, keys, chosen);
+  else
+    topk_by_sort(scores, n_blocks, top_k, keys, chosen);
   __syncthreads();
+  const int tid = static_cast<int>(threadIdx.x);
   if (tid < top_k) {
     const uint32_t me = chosen[tid];
     int rank = 0;
@@ -446,7 +486,7 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   s = pf::launch_status("pf_score_select (qsum)");
   if (s != PF_OK) return s;
   const double norm = 1.0 / (static_cast<double>(p.n_q) * n_c * p.H * sqrt(static_cast<double>(PF_HEAD_DIM)));
-  hipLaunchKernelGGL(score_kernel, dim3(n_blocks, n_batch), dim3(kScoreThreads), 0, st, ws, cf, qsum_off,
+  hipLaunchKernelGGL(score_kernel, dim3(n_blocks, n_batch), dim3((cols / 4 + 63) / 64 * 64), 0, st, ws, cf, qsum_off,
                      scores_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols, static_cast<float>(norm));
   s = pf::launch_status("pf_score_select (score)");
   if (s != PF_OK) return s;

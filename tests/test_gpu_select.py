@@ -87,6 +87,19 @@ def test_select_k_equals_m_and_limits():
     _compare({"q": q, "pool_k": pk[:2 * 1000]}, 2, 1)
 
 
+@pytest.mark.parametrize("heads", [1, 3, 5, 32])
+def test_select_head_counts(heads):
+    # one score thread per four columns, rounded up to whole waves: 1, 3 and 5
+    # heads leave part of the last wave without columns
+    say(f"test_select_head_counts heads={heads}")
+    rng = np.random.default_rng(100 + heads)
+    n_c, M = 20, 24
+    q = O.f64_to_bf16(rng.standard_normal((150, heads, 128)) + rng.standard_normal((1, heads, 128)))
+    off = np.repeat(rng.standard_normal((M, 1, heads, 128)) * 0.5, n_c, axis=1).reshape(-1, heads, 128)
+    pk = O.f64_to_bf16(rng.standard_normal((M * n_c, heads, 128)) + off)
+    _compare({"q": q, "pool_k": pk}, n_c, 6)
+
+
 def test_select_repeatable_bits():
     say("test_select_repeatable_bits")
     cfg = pfgen.C1
