@@ -250,6 +250,28 @@ def hbm_batched(pf, torch, cfg_pool, layers, reps):
                          "GB/s": round(sink_bytes / (ts * 1e-3) / 1e9, 1),
                          "frac_hbm": round(sink_bytes / (ts * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del sink
+    # The shift reads and writes whole 128-byte lines: the first line of each
+    # 256-byte row-head holds the 88 bytes of temporal dims, so 256 bytes move
+    # per 176 algorithmic (a layout ceiling of 68.75% of peak). Its line rate
+    # is set against a plain device copy (read + write) measured here.
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(7)]
+    for e in cev:
+        e[0].record(stream)
+        b.copy_(a)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    tc = float(np.median([e[0].elapsed_time(e[1]) for e in cev[2:]]))
+    copy_gbs = 2 * a.numel() / (tc * 1e-3) / 1e9
+    del a, b
+    out["copy_reference"] = {"workload": "1 GiB device copy (torch copy_), bytes read + written",
+                             "ms": round(tc, 4), "GB/s": round(copy_gbs, 1),
+                             "frac_hbm": round(copy_gbs / PEAK_HBM_GBS, 4)}
+    for key in ("rope_shift", "sink_shift"):
+        line = out[key]["GB/s"] * 256 / 176
+        out[key]["line_GB/s"] = round(line, 1)
+        out[key]["line_frac_of_copy"] = round(line / copy_gbs, 4)
     return out
 
 

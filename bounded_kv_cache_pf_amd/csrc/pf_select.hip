@@ -8,16 +8,19 @@
 // adjustment"; openbayes summary, "Method"]: the selected blocks are laid end to
 // end before the recent block and each one's temporal shift is returned.
 //
-// The scoring reads Q and the whole pool once (HBM-bound), in four launches on
-// one stream; every launch covers a batch of independent caches (grid y):
-//   1. colsum: every workgroup sums a segment of rows (a 64-row slice of Q, or a
+// The scoring reads Q and the whole pool once (HBM-bound), in three or four
+// launches on one stream; every launch covers a batch of independent caches
+// (grid y):
+//   1. colsum: every workgroup sums a segment of rows (a 32-row slice of Q, or a
 //      slice of one pool block) column by column into fp32 partials;
 //   2. qsum:   the Q partials are added per column, 16 interleaved runs of
 //              segments combined in a fixed order;
 //   3. score:  one workgroup per block adds its slices and dots with the Q sum;
 //   4. topk:   one workgroup per cache ranks (score desc, index asc) the keys
 //              in LDS, writes the first k ids in ascending order and, for the
-//              fused select-and-place call, places them.
+//              fused select-and-place call, places them. A small call (one
+//              layer) runs this in the last score workgroup of each cache
+//              instead of a fourth launch.
 // Every sum runs in a fixed order that does not depend on the batch, so
 // identical blocks get identical scores, repeated calls give identical bits,
 // and a batched call gives the bits of the single calls.
@@ -36,6 +39,7 @@ constexpr int kTargetSegments = 256;   // pool slices aimed at per cache (at lea
 constexpr int kRowUnroll = 4;      // rows whose loads a colsum thread keeps in flight
 constexpr int kQsumCols = 64;      // columns per qsum workgroup
 constexpr int kQsumRuns = 16;      // interleaved runs of Q segments per column
+constexpr int kFusedTopkMaxWorkgroups = 512;   // score launches up to this size also run the top-k
 
 struct SelectPlan {
   int H, cw;          // heads, 16-byte column chunks per row (H*16)
@@ -46,7 +50,7 @@ struct SelectPlan {
   int ksub;           // slices per pool block
   int sub_rows;       // rows per slice (last slice may be shorter)
   int n_seg;          // segments per cache
-  size_t cache_partials, cache_floats;   // floats per cache: partials, then qsum, then scores
+  size_t cache_partials, cache_floats;   // floats per cache: partials, qsum, scores, a counter
   size_t bytes;
 };
 
@@ -73,7 +77,7 @@ SelectPlan make_plan(int64_t n_q, int H, int n_blocks, int n_c, int n_batch, int
   p.n_seg = p.nq_seg + n_blocks * p.ksub;
   const size_t cols = static_cast<size_t>(H) * PF_HEAD_DIM;
   p.cache_partials = static_cast<size_t>(p.n_seg) * cols;
-  p.cache_floats = p.cache_partials + cols + static_cast<size_t>(n_blocks);
+  p.cache_floats = p.cache_partials + cols + static_cast<size_t>(n_blocks) + 1;
   p.cache_floats = (p.cache_floats + 63) & ~static_cast<size_t>(63);   // 256-byte aligned per cache
   p.bytes = p.cache_floats * sizeof(float) * static_cast<size_t>(n_batch);
   return p;
@@ -88,12 +92,15 @@ __global__ __launch_bounds__(1024) void colsum_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ pool, int64_t pool_bstride,
                                                       float* __restrict__ ws, int64_t cache_floats, int64_t n_q,
                                                       int nq_seg, int n_c, int ksub, int sub_rows,
-                                                      int64_t row_elems, int q_step, int head_step) {
+                                                      int64_t row_elems, int q_step, int head_step,
+                                                      int64_t counter_off) {
   extern __shared__ float red[];   // [rpar][cw*8]
   const int cw = blockDim.x, rpar = blockDim.y;
   const int x = threadIdx.x, y = threadIdx.y;
   const int seg = blockIdx.x;
   const int64_t b = blockIdx.y;
+  // the score launch counts its finished workgroups here (one counter per cache)
+  if (seg == 0 && x == 0 && y == 0) reinterpret_cast<uint32_t*>(ws + b * cache_floats + counter_off)[0] = 0u;
   const uint16_t* base;
   int64_t rows, stride;   // rows of this segment, elements between them
   if (seg < nq_seg) {
@@ -208,67 +215,10 @@ __device__ __forceinline__ void place_one(int32_t id, int r, int top_k, int32_t*
   tags[id] = target;
 }
 
-// 3. Block score: one workgroup per pool block and cache, one thread per four
-// columns (cols / 4 threads, rounded up to whole waves). A thread adds its columns' slices in slice
-// order (every load issued before the first add), dots them with the Q sum
-// in column order, and the threads' products are added by a fixed tree:
-// within each wave by lane-distance halving, then the waves in order.
-__global__ __launch_bounds__(1024) void score_kernel(float* __restrict__ ws, int64_t cache_floats,
-                                                     int64_t qsum_off, int64_t scores_off,
-                                                     float* __restrict__ scores_out, int n_blocks, int nq_seg,
-                                                     int ksub, int cols, float norm) {
-  __shared__ float red[16];
-  const int blk = blockIdx.x;
-  const int t = threadIdx.x;
-  const float* cache = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
-  const float4* kp =
-      reinterpret_cast<const float4*>(cache + (static_cast<int64_t>(nq_seg) + static_cast<int64_t>(blk) * ksub) * cols) + t;
-  const int c4 = cols >> 2;
-  float dot = 0.f;
-  if (t < c4) {
-    float4 ks = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = 0;
-    for (; s + 7 < ksub; s += 8) {
-      float4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = kp[static_cast<int64_t>(s + u) * c4];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        ks.x += v[u].x; ks.y += v[u].y; ks.z += v[u].z; ks.w += v[u].w;
-      }
-    }
-    for (; s < ksub; ++s) {
-      const float4 v = kp[static_cast<int64_t>(s) * c4];
-      ks.x += v.x; ks.y += v.y; ks.z += v.z; ks.w += v.w;
-    }
-    const float4 qv = reinterpret_cast<const float4*>(cache + qsum_off)[t];
-    dot = qv.x * ks.x;
-    dot += qv.y * ks.y;
-    dot += qv.z * ks.z;
-    dot += qv.w * ks.w;
-  }
-  // every lane of the (whole) waves takes part; lanes past the columns add 0
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) dot += __shfl_xor(dot, d);
-  const int n_waves = (blockDim.x + 63) >> 6;
-  if ((t & 63) == 0) red[t >> 6] = dot;
-  __syncthreads();
-  if (t == 0) {
-    float total = red[0];
-    for (int w = 1; w < n_waves; ++w) total += red[w];
-    const float sc = total * norm;
-    float* cw = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
-    cw[scores_off + blk] = sc;
-    if (scores_out) scores_out[static_cast<int64_t>(blockIdx.y) * n_blocks + blk] = sc;
-  }
-}
-
-// 4. Top-k, one workgroup per cache: the k smallest rank keys, written in
-// ascending id order; with tags != nullptr it also places the selected blocks.
-// Up to one key per thread, a key's rank is the count of smaller keys (all
-// keys differ, the index breaks ties); more blocks than threads are sorted
+// Top-k of one cache's scores by one workgroup: the k smallest rank keys. Up
+// to one key per thread, a key's rank is the count of smaller keys (all keys
+// differ, the index breaks ties); more blocks than threads are sorted
 // (bitonic, in LDS).
-constexpr int kTopkThreads = 1024;
 
 // chosen[r] = index of the key of rank r, r < top_k
 __device__ __forceinline__ void topk_by_rank(const float* scores, int n_blocks, int top_k, uint64_t* keys,
@@ -310,9 +260,122 @@ __device__ __forceinline__ void topk_by_sort(const float* scores, int n_blocks, 
       __syncthreads();
     }
   }
-  const int tid = static_cast<int>(threadIdx.x);
-  if (tid < top_k) chosen[tid] = static_cast<uint32_t>(keys[tid] & 0xFFFFFFFFu);
+  for (int r = threadIdx.x; r < top_k; r += blockDim.x) chosen[r] = static_cast<uint32_t>(keys[r] & 0xFFFFFFFFu);
 }
+
+
+// The k smallest rank keys of one cache's scores (by the calling workgroup),
+// written as ids in ascending order; with tags != nullptr those blocks are also
+// placed. keys, chosen and sorted_ids are the workgroup's LDS arrays.
+__device__ __forceinline__ void topk_write_place(const float* scores, int64_t b, int n_blocks, int top_k,
+                                                 int32_t* ids_out, int32_t* tags, int32_t recent_first_frame,
+                                                 int32_t block_frames, int32_t* deltas, uint64_t* keys,
+                                                 uint32_t* chosen, int32_t* sorted_ids) {
+  if (n_blocks <= static_cast<int>(blockDim.x))
+    topk_by_rank(scores, n_blocks, top_k, keys, chosen);
+  else
+    topk_by_sort(scores, n_blocks, top_k, keys, chosen);
+  __syncthreads();
+  // ascending ids: each chosen id's position is the count of smaller chosen ids
+  int32_t* ids = ids_out + b * top_k;
+  for (int i = threadIdx.x; i < top_k; i += blockDim.x) {
+    const uint32_t me = chosen[i];
+    int rank = 0;
+    for (int r = 0; r < top_k; ++r) rank += chosen[r] < me;
+    ids[rank] = static_cast<int32_t>(me);
+    sorted_ids[rank] = static_cast<int32_t>(me);
+  }
+  if (tags == nullptr) return;
+  __syncthreads();
+  for (int i = threadIdx.x; i < top_k; i += blockDim.x)
+    place_one(sorted_ids[i], i, top_k, tags + b * n_blocks, n_blocks, recent_first_frame, block_frames,
+              deltas + b * top_k + i);
+}
+
+// 3. Block score: one workgroup per pool block and cache, one thread per four
+// columns (cols / 4 threads, rounded up to whole waves). A thread adds its
+// columns' slices in slice order (every load issued before the first add),
+// dots them with the Q sum in column order, and the threads' products are
+// added by a fixed tree: within each wave by lane-distance halving, then the
+// waves in order.
+// kFused: the last workgroup of a cache to finish (a counter that the
+// column-sum launch cleared) also runs that cache's top-k and placement. Each
+// workgroup then publishes its score with a device-scope release, which
+// writes back its L2: cheap for a few dozen workgroups (one layer's call),
+// costly for thousands (a batched call), which launch topk_kernel instead.
+template <bool kFused>
+__global__ __launch_bounds__(1024) void score_kernel(float* __restrict__ ws, int64_t cache_floats, int64_t qsum_off,
+                                                     int64_t scores_off, int64_t counter_off,
+                                                     float* __restrict__ scores_out, int n_blocks, int nq_seg,
+                                                     int ksub, int cols, float norm, int top_k,
+                                                     int32_t* __restrict__ ids_out, int32_t* __restrict__ tags,
+                                                     int32_t recent_first_frame, int32_t block_frames,
+                                                     int32_t* __restrict__ deltas) {
+  __shared__ float red[16];
+  __shared__ uint64_t keys[kFused ? PF_MAX_BLOCKS : 1];
+  __shared__ uint32_t chosen[kFused ? PF_MAX_TOPK : 1];
+  __shared__ int32_t sorted_ids[kFused ? PF_MAX_TOPK : 1];
+  __shared__ int is_last;
+  const int blk = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.y;
+  float* cache = ws + b * cache_floats;
+  const float4* kp =
+      reinterpret_cast<const float4*>(cache + (static_cast<int64_t>(nq_seg) + static_cast<int64_t>(blk) * ksub) * cols) + t;
+  const int c4 = cols >> 2;
+  float dot = 0.f;
+  if (t < c4) {
+    float4 ks = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = 0;
+    for (; s + 7 < ksub; s += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = kp[static_cast<int64_t>(s + u) * c4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ks.x += v[u].x; ks.y += v[u].y; ks.z += v[u].z; ks.w += v[u].w;
+      }
+    }
+    for (; s < ksub; ++s) {
+      const float4 v = kp[static_cast<int64_t>(s) * c4];
+      ks.x += v.x; ks.y += v.y; ks.z += v.z; ks.w += v.w;
+    }
+    const float4 qv = reinterpret_cast<const float4*>(cache + qsum_off)[t];
+    dot = qv.x * ks.x;
+    dot += qv.y * ks.y;
+    dot += qv.z * ks.z;
+    dot += qv.w * ks.w;
+  }
+  // every lane of the (whole) waves takes part; lanes past the columns add 0
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) dot += __shfl_xor(dot, d);
+  const int n_waves = (blockDim.x + 63) >> 6;
+  if ((t & 63) == 0) red[t >> 6] = dot;
+  __syncthreads();
+  if (t == 0) {
+    float total = red[0];
+    for (int w = 1; w < n_waves; ++w) total += red[w];
+    const float sc = total * norm;
+    cache[scores_off + blk] = sc;
+    if (scores_out) scores_out[b * n_blocks + blk] = sc;
+    if constexpr (kFused) {
+      // release the score, then count this workgroup
+      __threadfence();
+      const uint32_t done = atomicAdd(reinterpret_cast<uint32_t*>(cache + counter_off), 1u);
+      is_last = done == static_cast<uint32_t>(n_blocks - 1);
+    }
+  }
+  if constexpr (kFused) {
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();   // acquire: every workgroup's score is visible from here
+    topk_write_place(cache + scores_off, b, n_blocks, top_k, ids_out, tags, recent_first_frame, block_frames,
+                     deltas, keys, chosen, sorted_ids);
+  }
+}
+
+// 4. Top-k (batched calls): one workgroup per cache.
+constexpr int kTopkThreads = 1024;
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ ws, int64_t cache_floats,
                                                              int64_t scores_off, int n_blocks, int top_k,
@@ -323,26 +386,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   __shared__ uint32_t chosen[PF_MAX_TOPK];
   __shared__ int32_t sorted_ids[PF_MAX_TOPK];
   const int64_t b = blockIdx.x;
-  const float* scores = ws + b * cache_floats + scores_off;
-  int32_t* ids = ids_out + b * top_k;
-  if (n_blocks <= kTopkThreads)
-    topk_by_rank(scores, n_blocks, top_k, keys, chosen);
-  else
-    topk_by_sort(scores, n_blocks, top_k, keys, chosen);
-  __syncthreads();
-  const int tid = static_cast<int>(threadIdx.x);
-  if (tid < top_k) {
-    const uint32_t me = chosen[tid];
-    int rank = 0;
-    for (int r = 0; r < top_k; ++r) rank += chosen[r] < me;
-    ids[rank] = static_cast<int32_t>(me);
-    sorted_ids[rank] = static_cast<int32_t>(me);
-  }
-  if (tags == nullptr) return;
-  __syncthreads();
-  if (tid < top_k)
-    place_one(sorted_ids[tid], tid, top_k, tags + b * n_blocks, n_blocks, recent_first_frame, block_frames,
-              deltas + b * top_k + tid);
+  topk_write_place(ws + b * cache_floats + scores_off, b, n_blocks, top_k, ids_out, tags, recent_first_frame,
+                   block_frames, deltas, keys, chosen, sorted_ids);
 }
 
 // Placement, one workgroup per cache.
@@ -471,6 +516,7 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   const int64_t cf = static_cast<int64_t>(p.cache_floats);
   const int64_t qsum_off = static_cast<int64_t>(p.cache_partials);
   const int64_t scores_off = qsum_off + cols;
+  const int64_t counter_off = scores_off + n_blocks;
   const int64_t qs = n_batch > 1 ? q_batch_stride : 0;
   const int64_t ps = n_batch > 1 ? pool_batch_stride : 0;
 
@@ -478,7 +524,7 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   hipLaunchKernelGGL(colsum_kernel, dim3(p.n_seg, n_batch), dim3(p.cw, p.rpar), lds, st,
                      reinterpret_cast<const uint16_t*>(q), qs, reinterpret_cast<const uint16_t*>(pool_k), ps, ws,
                      cf, p.n_q, p.nq_seg, n_c, p.ksub, p.sub_rows, static_cast<int64_t>(n_heads) * PF_HEAD_DIM,
-                     q_step, head_step);
+                     q_step, head_step, counter_off);
   pf_status s = pf::launch_status("pf_score_select (colsum)");
   if (s != PF_OK) return s;
   hipLaunchKernelGGL(qsum_kernel, dim3((cols + kQsumCols - 1) / kQsumCols, n_batch), dim3(kQsumCols * kQsumRuns), 0,
@@ -486,13 +532,21 @@ pf_status score_select(const pf_bf16* q, int64_t q_batch_stride, int64_t n_q, in
   s = pf::launch_status("pf_score_select (qsum)");
   if (s != PF_OK) return s;
   const double norm = 1.0 / (static_cast<double>(p.n_q) * n_c * p.H * sqrt(static_cast<double>(PF_HEAD_DIM)));
-  hipLaunchKernelGGL(score_kernel, dim3(n_blocks, n_batch), dim3((cols / 4 + 63) / 64 * 64), 0, st, ws, cf, qsum_off,
-                     scores_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols, static_cast<float>(norm));
+  const dim3 score_threads((cols / 4 + 63) / 64 * 64);
+  if (static_cast<int64_t>(n_blocks) * n_batch <= kFusedTopkMaxWorkgroups) {
+    hipLaunchKernelGGL(score_kernel<true>, dim3(n_blocks, n_batch), score_threads, 0, st, ws, cf, qsum_off,
+                       scores_off, counter_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols,
+                       static_cast<float>(norm), top_k, ids_out, tags, recent_first_frame, block_frames, deltas_out);
+    return pf::launch_status("pf_score_select (score, top-k)");
+  }
+  hipLaunchKernelGGL(score_kernel<false>, dim3(n_blocks, n_batch), score_threads, 0, st, ws, cf, qsum_off,
+                     scores_off, counter_off, scores_out, n_blocks, p.nq_seg, p.ksub, cols, static_cast<float>(norm),
+                     top_k, ids_out, tags, recent_first_frame, block_frames, deltas_out);
   s = pf::launch_status("pf_score_select (score)");
   if (s != PF_OK) return s;
   hipLaunchKernelGGL(topk_kernel, dim3(n_batch), dim3(kTopkThreads), 0, st, ws, cf, scores_off, n_blocks, top_k,
                      ids_out, tags, recent_first_frame, block_frames, deltas_out);
-  return pf::launch_status("pf_score_select (topk)");
+  return pf::launch_status("pf_score_select (top-k)");
 }
 
 }  // namespace

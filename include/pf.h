@@ -188,9 +188,9 @@ pf_status pf_selection_deltas_batched(const int32_t* ids, int top_k, int32_t* po
  *  adjustment"]
  *
  * Same results as pf_score_select followed by pf_selection_deltas with the same
- * arguments (ids, deltas, updated pos_tags and scores are bit-identical), in
- * four launches instead of five: the workgroup that selects a cache's top-k
- * also places them. Workspace: pf_score_select_workspace_bytes
+ * arguments (ids, deltas, updated pos_tags and scores are bit-identical), with
+ * one launch fewer: the workgroup that selects a cache's top-k also places
+ * them. Workspace: pf_score_select_workspace_bytes
  * (batched: pf_score_select_batched_workspace_bytes); concurrent calls must not
  * share a workspace. Arguments and limits as for the two calls; pos_tags and
  * deltas_out must not be NULL.

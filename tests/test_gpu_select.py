@@ -87,13 +87,16 @@ def test_select_k_equals_m_and_limits():
     _compare({"q": q, "pool_k": pk[:2 * 1000]}, 2, 1)
 
 
-@pytest.mark.parametrize("heads", [1, 3, 5, 32])
-def test_select_head_counts(heads):
+@pytest.mark.parametrize("heads,M", [(1, 24), (3, 24), (5, 24), (32, 24), (1, 300), (2, 700)])
+def test_select_head_counts(heads, M):
     # one score thread per four columns, rounded up to whole waves: 1, 3 and 5
-    # heads leave part of the last wave without columns
-    say(f"test_select_head_counts heads={heads}")
-    rng = np.random.default_rng(100 + heads)
-    n_c, M = 20, 24
+    # heads leave part of the last wave without columns. A one-layer call with
+    # at most 512 blocks ranks in its last score workgroup, by counting when
+    # the blocks fit one per thread and by sorting when they do not (1 head,
+    # 300 blocks); 700 blocks take the separate top-k launch.
+    say(f"test_select_head_counts heads={heads} M={M}")
+    rng = np.random.default_rng(100 + heads + M)
+    n_c = 20 if M < 100 else 4
     q = O.f64_to_bf16(rng.standard_normal((150, heads, 128)) + rng.standard_normal((1, heads, 128)))
     off = np.repeat(rng.standard_normal((M, 1, heads, 128)) * 0.5, n_c, axis=1).reshape(-1, heads, 128)
     pk = O.f64_to_bf16(rng.standard_normal((M * n_c, heads, 128)) + off)
