@@ -211,10 +211,12 @@ def test_select_place_fused_equals_separate_calls(cfg):
         assert t_fused.cpu().numpy().tolist() == t_ref.tolist()
 
 
-def test_select_place_batched_equals_single_calls():
-    say("test_select_place_batched_equals_single_calls")
+@pytest.mark.parametrize("B", [4, 6])
+def test_select_place_batched_equals_single_calls(B):
+    # 4 caches x 116 blocks rank in their last score workgroups; 6 caches
+    # (696 score workgroups) take the separate top-k launch
+    say(f"test_select_place_batched_equals_single_calls B={B}")
     cfg = pfgen.C2
-    B = 4
     cs = [pfgen.make(cfg, cfg.seed + 60 + b) for b in range(B)]
     M, k, Bf = cfg.pool_blocks, cfg.top_k, cfg.block_frames
     fr = (cfg.sink_blocks + M) * Bf
