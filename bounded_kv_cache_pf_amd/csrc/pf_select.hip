@@ -170,18 +170,19 @@ __global__ __launch_bounds__(kQsumCols * kQsumRuns) void qsum_kernel(float* __re
   float* cache = ws + static_cast<int64_t>(blockIdx.y) * cache_floats;
   float s = 0.f;
   if (c < cols) {
-    int i = g;
-    for (; i + 3 * kQsumRuns < nq_seg; i += 4 * kQsumRuns) {
-      const float a0 = cache[static_cast<int64_t>(i) * cols + c];
-      const float a1 = cache[static_cast<int64_t>(i + kQsumRuns) * cols + c];
-      const float a2 = cache[static_cast<int64_t>(i + 2 * kQsumRuns) * cols + c];
-      const float a3 = cache[static_cast<int64_t>(i + 3 * kQsumRuns) * cols + c];
-      s += a0;
-      s += a1;
-      s += a2;
-      s += a3;
+    // eight segments per pass, all loaded before the first add (a segment past
+    // the last reads segment g and adds 0), so a pass costs one memory latency
+    constexpr int kPass = 8;
+    for (int i = g; i < nq_seg; i += kPass * kQsumRuns) {
+      float v[kPass];
+#pragma unroll
+      for (int u = 0; u < kPass; ++u) {
+        const int seg = i + u * kQsumRuns;
+        v[u] = cache[static_cast<int64_t>(seg < nq_seg ? seg : g) * cols + c];
+      }
+#pragma unroll
+      for (int u = 0; u < kPass; ++u) s += i + u * kQsumRuns < nq_seg ? v[u] : 0.f;
     }
-    for (; i < nq_seg; i += kQsumRuns) s += cache[static_cast<int64_t>(i) * cols + c];
   }
   red[g][tc] = s;
   __syncthreads();
