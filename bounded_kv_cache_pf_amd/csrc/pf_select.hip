@@ -11,7 +11,7 @@
 // The scoring reads Q and the whole pool once (HBM-bound), in three or four
 // launches on one stream; every launch covers a batch of independent caches
 // (grid y):
-//   1. colsum: every workgroup sums a segment of rows (a 32-row slice of Q, or a
+//   1. colsum: every workgroup sums a segment of rows (a 64-row slice of Q, or a
 //      slice of one pool block) column by column into fp32 partials;
 //   2. qsum:   the Q partials are added per column, 16 interleaved runs of
 //              segments combined in a fixed order;
@@ -31,11 +31,16 @@
 namespace {
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));   // for the streaming (non-temporal) loads
 
-// rows of Q per colsum workgroup: short, so that one cache's queries spread over
-// as many workgroups as its pool slices; the same for every batch size, so a
-// batched call adds in the order of the single calls
-constexpr int kQSegRows = 32;
-constexpr int kTargetSegments = 256;   // pool slices aimed at per cache (at least one per block)
+// Segments of the column sums, the same for every batch size, so a batched call
+// adds in the order of the single calls. Q rows per colsum workgroup, and the
+// pool slices aimed at per cache (at least one per block): one layer's call
+// (6,240 queries, 40 blocks) gets 98 Q and 120 pool workgroups, about one per
+// CU; a 116-block pool gets one slice per block, a third of the partial sums
+// that the score kernel reads back before. Timed on one device against 32 /
+// 256 and other pairs: 2.5 us faster for one layer, 11% faster for 30 caches
+// batched.
+constexpr int kQSegRows = 64;
+constexpr int kTargetSegments = 96;
 constexpr int kRowUnroll = 4;      // rows whose loads a colsum thread keeps in flight
 constexpr int kQsumCols = 64;      // columns per qsum workgroup
 constexpr int kQsumRuns = 16;      // interleaved runs of Q segments per column
