@@ -26,8 +26,13 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLanesPerRowHead = 8;
 constexpr int kRowHeadsPerPass = kThreads / kLanesPerRowHead;  // 32
-constexpr int kPasses = 4;
-constexpr int kRowHeadsPerBlock = kRowHeadsPerPass * kPasses;  // 128 per workgroup
+// Row-heads per lane: four keep 64 KB of each large launch in flight per
+// workgroup; a small launch (one layer's selected blocks) takes two, twice the
+// workgroups, each with a shorter chain of loads, rotations and stores
+// (1.2 us faster for one layer, 10% slower on 30 layers' blocks).
+constexpr int kPassesLarge = 4;
+constexpr int kPassesSmall = 2;
+constexpr int64_t kSmallLaunchRowHeads = int64_t{1} << 17;
 constexpr int kPairs = PF_TEMPORAL_DIMS / 2;                   // 22
 
 // fp64 -> bf16 with a single round-to-nearest-even. The hardware fp64 -> fp32
@@ -52,6 +57,7 @@ __device__ __forceinline__ void rotate_pair(uint32_t& packed, double c, double s
   packed = f64_to_bf16_rne(xr) | (f64_to_bf16_rne(yr) << 16);
 }
 
+template <int kPasses>
 __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
     uint16_t* __restrict__ k, int64_t k_bstride, int64_t row_heads_per_block, int64_t n_blocks,
     const int32_t* __restrict__ block_ids, const int32_t* __restrict__ deltas, int n_shift, double base) {
@@ -63,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void rope_shift_kernel(
   const int sub = threadIdx.x % kLanesPerRowHead;
   const int local = threadIdx.x / kLanesPerRowHead;
   uint16_t* blk_base = k + blockIdx.z * k_bstride + blk * row_heads_per_block * PF_HEAD_DIM;
+  constexpr int kRowHeadsPerBlock = kRowHeadsPerPass * kPasses;
   const int64_t rh0 = static_cast<int64_t>(blockIdx.x) * kRowHeadsPerBlock + local;
   // all loads first (kPasses row-heads in flight per lane), then rotate and store
   uint4 w[kPasses];
@@ -133,12 +140,19 @@ extern "C" pf_status pf_rope_shift_batched(pf_bf16* k, int64_t k_batch_stride, i
   PF_REQUIRE((reinterpret_cast<uintptr_t>(block_ids) & 3u) == 0, PF_ERR_MISALIGNED, "block_ids is not 4-byte aligned");
 
   const int64_t rh_per_block = rows_per_block * n_heads;
-  const int64_t gx = (rh_per_block + kRowHeadsPerBlock - 1) / kRowHeadsPerBlock;
+  const bool small = rh_per_block * n_shift * n_batch <= kSmallLaunchRowHeads;
+  const int64_t per_wg = kRowHeadsPerPass * (small ? kPassesSmall : kPassesLarge);
+  const int64_t gx = (rh_per_block + per_wg - 1) / per_wg;
   PF_REQUIRE(gx <= 0x7FFFFFFF, PF_ERR_UNSUPPORTED, "block too large");
   dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(n_shift), static_cast<unsigned>(n_batch));
-  hipLaunchKernelGGL(rope_shift_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     reinterpret_cast<uint16_t*>(k), n_batch > 1 ? k_batch_stride : 0, rh_per_block, n_blocks,
-                     block_ids, deltas, n_shift, rope_base);
+  if (small)
+    hipLaunchKernelGGL(rope_shift_kernel<kPassesSmall>, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       reinterpret_cast<uint16_t*>(k), n_batch > 1 ? k_batch_stride : 0, rh_per_block, n_blocks,
+                       block_ids, deltas, n_shift, rope_base);
+  else
+    hipLaunchKernelGGL(rope_shift_kernel<kPassesLarge>, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       reinterpret_cast<uint16_t*>(k), n_batch > 1 ? k_batch_stride : 0, rh_per_block, n_blocks,
+                       block_ids, deltas, n_shift, rope_base);
   return pf::launch_status("pf_rope_shift");
 }
 
