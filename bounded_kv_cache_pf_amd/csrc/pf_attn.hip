@@ -37,11 +37,17 @@
 //  * Scheduling: with G resident workgroups and U units, the first
 //    floor(U/G) rounds give every workgroup whole units, numbered so that each
 //    XCD walks consecutive units of one head in lockstep (shared K/V in its
-//    L2). The R remaining units are each cut into the same floor(G/R) key
-//    segments; neighbouring workgroups take the same segment of different
-//    units, so they too read the same keys together. Segments write
-//    unnormalised partial results that a small merge kernel combines. This
-//    removes the tail round of idle CUs.
+//    L2). The units of full query tiles come first and the heads' last,
+//    partial query tiles after them, so the partial ones fall in the tail.
+//    The R remaining units are cut into key segments, one segment count per
+//    kind of unit (full or partial), chosen so that the segments end close
+//    together: a wave whose 32 queries all lie past the last query only loads
+//    its share of each tile, which makes a partial unit with at most four live
+//    waves cheaper per tile. Neighbouring workgroups take the same segment of
+//    different full units, so they too read the same keys together; the
+//    partial units (one per head, none sharing keys) are spread over all
+//    XCDs. Segments write unnormalised partial results that a small merge
+//    kernel combines. This removes the tail round of idle CUs.
 #include <math.h>
 
 #include <mutex>
@@ -93,13 +99,13 @@ struct AttnArgs {
   int32_t n_sel;
   int32_t n_blocks;
   int32_t e_sink, e_mid, e_rec, e_cur;   // cumulative ends of the partitions (e_cur = key count)
-  int32_t num_qtiles;
-  int32_t units;            // num_qtiles * H
+  int32_t units;            // query units (ceil(n_q / kBM) per head) x H
   int32_t n_kt;             // key tiles per unit
   int32_t G;                // workgroups in the grid
   int32_t rounds;           // rounds of whole units
-  int32_t n_tail;           // units cut into key segments (after the whole rounds)
-  int32_t n_seg;            // segments per cut unit (1: the tail units run whole)
+  int32_t nfull;            // query units per head with kBM real queries
+  int32_t tail_f, tail_p;   // tail units with kBM real queries / with fewer
+  int32_t seg_f, seg_p;     // key segments per tail unit of each kind (1: it runs whole)
   float scale_log2;
   float inv_nc;             // 1 / n_c
 };
@@ -331,6 +337,21 @@ struct Smem {
   int any_bad_id;
 };
 
+// Units are numbered head-major over the full query units of every head
+// first, then the last, partial unit of each head (when n_q is not a
+// multiple of kBM), so that the partial units, which cost less, fall in the
+// tail where they get their own segment count.
+__device__ __forceinline__ void unit_coords(const AttnArgs& a, int unit, int& h, int64_t& q0) {
+  const int full = a.H * a.nfull;
+  if (unit < full) {
+    h = unit / a.nfull;
+    q0 = static_cast<int64_t>(unit - h * a.nfull) * kBM;
+  } else {
+    h = unit - full;
+    q0 = static_cast<int64_t>(a.nfull) * kBM;
+  }
+}
+
 // One unit (head h, queries q0 .. q0+kBM-1) over key tiles [kt0, kt1).
 // direct: the run covers the whole unit -> write O (and LSE); otherwise write
 // the unnormalised partial U, m (log2 domain) and l to partial slot `slot`.
@@ -346,6 +367,8 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
   // Q^T operand: query q0 + 32 wave + l32, dims 16 st + 8 g .. +7.
   const int64_t qrow = q0 + wave * 32 + l32;
   const bool qvalid = qrow < a.n_q;
+  // a wave whose queries all lie past n_q only loads its share of each tile
+  const bool live = q0 + 32 * wave_u < a.n_q;
   bf16x8 qf[8];
   {
     const uint16_t* qp = a.q + (qvalid ? qrow : 0) * a.row_stride + static_cast<int64_t>(h) * D + 8 * g;
@@ -408,6 +431,15 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, Smem& sm, int h, int
       spread = contiguous_tile(a, h, kt + 1, wave_u, lane, nt) ||
                mid_tile(a, sm.ids, h, kt + 1, wave_u, lane, kbad_next, nt);
       if (!spread) load_general(a, sm.ids, h, kt + 1, k_next, v_next, kbad_next, wave_u, lane);
+    }
+    if (!live) {
+      if (spread) {
+#pragma unroll
+        for (int j = 0; j < 2 * kLoadsPerWave; ++j) load_part(nt, j, k_next, v_next, wave_u);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      return;
     }
 
     // ---- S^T = K Q^T for kNB 32-key blocks ----
@@ -603,46 +635,86 @@ __global__ __launch_bounds__(kThreads, kOcc) void partition_attn_kernel(AttnArgs
   for (int r = 0; r < a.rounds; ++r) {
     const int unit = r * a.G + slot;
     if (unit >= a.units) break;
-    run_unit(a, sm, unit / a.num_qtiles, static_cast<int64_t>(unit % a.num_qtiles) * kBM, 0, a.n_kt, true, 0);
+    int h;
+    int64_t q0;
+    unit_coords(a, unit, h, q0);
+    run_unit(a, sm, h, q0, 0, a.n_kt, true, 0);
   }
-  // Tail: item i = segment i / n_tail of tail unit i % n_tail. Every tail unit
-  // is cut at the same key tiles and neighbouring slots (one XCD) take the same
-  // segment of different units, so they read the same keys at the same time
-  // and share them in that XCD's L2.
-  if (slot < a.n_seg * a.n_tail) {
-    const int seg = slot / a.n_tail;
-    const int tu = slot - seg * a.n_tail;
-    const int kt0 = static_cast<int>(static_cast<int64_t>(seg) * a.n_kt / a.n_seg);
-    const int kt1 = static_cast<int>(static_cast<int64_t>(seg + 1) * a.n_kt / a.n_seg);
-    const int unit = a.units - a.n_tail + tu;
-    run_unit(a, sm, unit / a.num_qtiles, static_cast<int64_t>(unit % a.num_qtiles) * kBM, kt0, kt1, a.n_seg == 1,
-             slot);
+  // Tail items: the segments of the full tail units (n_f of them, segment-
+  // major: item k is segment k / tail_f of unit k % tail_f), then those of the
+  // partial ones (n_p). Item k of the full kind writes partial slot k, item k
+  // of the partial kind slot n_f + k. The items are laid out in one sequence
+  // with the partial ones spread evenly among the full ones, and each XCD
+  // takes a run of consecutive positions: neighbouring workgroups take the
+  // same segment of different full units and share those keys in their XCD's
+  // L2, while the partial units, each alone with its keys, are spread over
+  // all XCDs.
+  const int n_f = a.seg_f * a.tail_f;
+  const int n_p = a.seg_p * a.tail_p;
+  const int n_items = n_f + n_p;
+  int pos = -1;
+  if (a.G % kXcds == 0) {
+    const int per = a.G / kXcds;
+    const int x = slot / per;
+    const int j = slot - x * per;
+    const int lo = static_cast<int>(static_cast<int64_t>(x) * n_items / kXcds);
+    const int hi = static_cast<int>(static_cast<int64_t>(x + 1) * n_items / kXcds);
+    if (j < hi - lo) pos = lo + j;
+  } else if (slot < n_items) {
+    pos = slot;
+  }
+  if (pos >= 0) {
+    const int p0 = static_cast<int>(static_cast<int64_t>(pos) * n_p / n_items);
+    const int p1 = static_cast<int>(static_cast<int64_t>(pos + 1) * n_p / n_items);
+    int seg, tu, nseg, buf;
+    if (p1 > p0) {
+      seg = p0 / a.tail_p;
+      tu = a.tail_f + p0 - seg * a.tail_p;
+      nseg = a.seg_p;
+      buf = n_f + p0;
+    } else {
+      const int k = pos - p0;
+      seg = k / a.tail_f;
+      tu = k - seg * a.tail_f;
+      nseg = a.seg_f;
+      buf = k;
+    }
+    const int kt0 = static_cast<int>(static_cast<int64_t>(seg) * a.n_kt / nseg);
+    const int kt1 = static_cast<int>(static_cast<int64_t>(seg + 1) * a.n_kt / nseg);
+    int h;
+    int64_t q0;
+    unit_coords(a, a.units - a.tail_f - a.tail_p + tu, h, q0);
+    run_unit(a, sm, h, q0, kt0, kt1, nseg == 1, buf);
   }
 }
 
 // Merge the segments of cut units. Workgroup (tu, y) takes queries
-// 32y .. 32y+31 of cut unit tu, whose segment s wrote partial slot
-// tu + s * n_tail; eight threads share a query, 16 dims each.
+// 32y .. 32y+31 of tail unit tu, whose segment c wrote partial slot
+// first + c * stride; eight threads share a query, 16 dims each.
 constexpr int kMergeQueries = 32;
 
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int tu = blockIdx.x;
-  const int unit = a.units - a.n_tail + tu;
-  const int h = unit / a.num_qtiles;
-  const int64_t q0 = static_cast<int64_t>(unit % a.num_qtiles) * kBM;
+  const bool kind_f = tu < a.tail_f;
+  const int nseg = kind_f ? a.seg_f : a.seg_p;
+  if (nseg <= 1) return;
+  const int64_t first = kind_f ? tu : static_cast<int64_t>(a.seg_f) * a.tail_f + (tu - a.tail_f);
+  const int64_t stride = kind_f ? a.tail_f : a.tail_p;
+  int h;
+  int64_t q0;
+  unit_coords(a, a.units - a.tail_f - a.tail_p + tu, h, q0);
   const int ql = blockIdx.y * kMergeQueries + (threadIdx.x >> 3);
   const int d0 = (threadIdx.x & 7) * 16;
   const int64_t qrow = q0 + ql;
   float m = -INFINITY;
-  for (int c = 0; c < a.n_seg; ++c)
-    m = fmaxf(m, a.part[(tu + static_cast<int64_t>(c) * a.n_tail) * kPartFloats + kBM * D + ql]);
+  for (int c = 0; c < nseg; ++c) m = fmaxf(m, a.part[(first + c * stride) * kPartFloats + kBM * D + ql]);
   const float m_use = m == -INFINITY ? 0.f : m;
   float l = 0.f;
   float u[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) u[i] = 0.f;
-  for (int c = 0; c < a.n_seg; ++c) {
-    const float* base = a.part + (tu + static_cast<int64_t>(c) * a.n_tail) * kPartFloats;
+  for (int c = 0; c < nseg; ++c) {
+    const float* base = a.part + (first + c * stride) * kPartFloats;
     const float w = __builtin_amdgcn_exp2f(base[kBM * D + ql] - m_use);
     l += w * base[kBM * D + kBM + ql];
     const float* up = base + static_cast<int64_t>(ql) * D + d0;
@@ -676,7 +748,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 
 struct Plan {
   int64_t units = 0, n_kt = 0;
-  int grid = 0, G = 0, rounds = 0, n_tail = 0, n_seg = 0;
+  int grid = 0, G = 0, rounds = 0, nfull = 0, tail_f = 0, tail_p = 0, seg_f = 0, seg_p = 0;
   size_t ws_bytes = 0;
 };
 
@@ -697,28 +769,58 @@ int resident_workgroups() {
   return cached[dev];
 }
 
-// rounds of whole units first; a remainder under 3/4 of the machine is cut
-// into as many equal key segments per unit as the machine holds (each at
-// least kMinTailTiles tiles), otherwise it runs as one more round of whole
-// units.
+// Cost of a key tile for a unit whose live waves each have a SIMD to
+// themselves (at most 4 of its 8 waves hold queries), relative to a unit whose
+// SIMDs each run two live waves. Measured on the default layer's shape (3 live
+// waves): cutting those units into 4 segments instead of 5 did not lengthen
+// the tail, so such a tile costs at most about 2/3 of a full one.
+constexpr double kLoneWaveCost = 0.75;
+
+// Rounds of whole units first; a remainder under 3/4 of the machine is cut
+// into key segments (each at least kMinTailTiles tiles), otherwise it runs as
+// one more round of whole units. The tail holds up to two kinds of unit: full
+// ones, and the partial last units of the heads, which cost less per tile
+// when at most four of their waves hold queries. Each kind gets one segment
+// count; the dearer kind (longest segment x cost) gets one more segment per
+// unit while the machine holds them, so the slots end close to together.
 Plan make_plan(int64_t n_q, int H, int64_t n_keys, int resident) {
   Plan p;
-  p.units = ((n_q + kBM - 1) / kBM) * H;
+  p.nfull = static_cast<int>(n_q / kBM);
+  const int64_t rest = n_q - static_cast<int64_t>(p.nfull) * kBM;
+  p.units = (static_cast<int64_t>(p.nfull) + (rest > 0 ? 1 : 0)) * H;
   p.n_kt = (n_keys + kBN - 1) / kBN;
   const int64_t full = p.units / resident;
   const int64_t rem = p.units - full * resident;
   p.rounds = static_cast<int>(full);
   if (rem > 0 && (rem * 4 < static_cast<int64_t>(resident) * 3 || full == 0)) {
-    p.n_tail = static_cast<int>(rem);
-    int64_t seg = resident / rem;
-    if (seg > p.n_kt / kMinTailTiles) seg = p.n_kt / kMinTailTiles;
-    if (seg < 1) seg = 1;
-    p.n_seg = static_cast<int>(seg);
-    p.ws_bytes = seg > 1 ? static_cast<size_t>(seg * rem) * kPartBytes : 0;
-  } else if (rem > 0) {
-    p.rounds += 1;
+    const int64_t partial_units = rest > 0 ? H : 0;
+    p.tail_p = static_cast<int>(rem < partial_units ? rem : partial_units);
+    p.tail_f = static_cast<int>(rem - p.tail_p);
+    const double cost_p = (rest + 31) / 32 <= 4 ? kLoneWaveCost : 1.0;
+    int64_t max_seg = p.n_kt / kMinTailTiles;
+    if (max_seg < 1) max_seg = 1;
+    p.seg_f = p.tail_f > 0 ? 1 : 0;
+    p.seg_p = p.tail_p > 0 ? 1 : 0;
+    int64_t used = rem;
+    for (;;) {
+      const double len_f = p.tail_f > 0 ? static_cast<double>(p.n_kt) / p.seg_f : 0.0;
+      const double len_p = p.tail_p > 0 ? cost_p * static_cast<double>(p.n_kt) / p.seg_p : 0.0;
+      const bool inc_f = p.tail_f > 0 && len_f >= len_p;
+      const bool inc_p = p.tail_p > 0 && len_p >= len_f;
+      const int64_t need = (inc_f ? p.tail_f : 0) + (inc_p ? p.tail_p : 0);
+      if (used + need > resident) break;
+      if ((inc_f && p.seg_f + 1 > max_seg) || (inc_p && p.seg_p + 1 > max_seg)) break;
+      p.seg_f += inc_f ? 1 : 0;
+      p.seg_p += inc_p ? 1 : 0;
+      used += need;
+    }
+    const int64_t slots = static_cast<int64_t>(p.seg_f) * p.tail_f + static_cast<int64_t>(p.seg_p) * p.tail_p;
+    p.ws_bytes = (p.seg_f > 1 || p.seg_p > 1) ? static_cast<size_t>(slots) * kPartBytes : 0;
+    p.grid = full > 0 ? resident : static_cast<int>(slots);
+  } else {
+    if (rem > 0) p.rounds += 1;
+    p.grid = full > 0 ? resident : static_cast<int>(rem);
   }
-  p.grid = full > 0 ? resident : p.n_seg * p.n_tail;
   p.G = p.grid;
   return p;
 }
@@ -872,21 +974,23 @@ pf_status attn_call(const pf_bf16* q, int64_t n_q, int n_heads, const pf_bf16* s
   a.e_mid = static_cast<int32_t>(n_sink + n_mid);
   a.e_rec = static_cast<int32_t>(n_sink + n_mid + n_recent);
   a.e_cur = static_cast<int32_t>(n_keys);
-  a.num_qtiles = static_cast<int32_t>(num_qtiles);
   a.units = static_cast<int32_t>(p.units);
   a.n_kt = static_cast<int32_t>(p.n_kt);
   a.G = p.G;
   a.rounds = p.rounds;
-  a.n_tail = p.n_tail;
-  a.n_seg = p.n_seg;
+  a.nfull = p.nfull;
+  a.tail_f = p.tail_f;
+  a.tail_p = p.tail_p;
+  a.seg_f = p.seg_f;
+  a.seg_p = p.seg_p;
   const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(D));
   a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(partition_attn_kernel, dim3(p.grid), dim3(kThreads), 0, st, a);
   pf_status s = pf::launch_status("pf_partition_attn");
-  if (s != PF_OK || p.n_seg <= 1) return s;
-  hipLaunchKernelGGL(merge_kernel, dim3(p.n_tail, kBM / kMergeQueries), dim3(256), 0, st, a);
+  if (s != PF_OK || (p.seg_f <= 1 && p.seg_p <= 1)) return s;
+  hipLaunchKernelGGL(merge_kernel, dim3(p.tail_f + p.tail_p, kBM / kMergeQueries), dim3(256), 0, st, a);
   return pf::launch_status("pf_partition_attn (merge)");
 }
 

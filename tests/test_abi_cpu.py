@@ -181,6 +181,30 @@ def test_attn_validation(pf):
     assert _err(pf, _attn(pf, ws=C + 8, wsb=need))[0] == "PF_ERR_MISALIGNED"
 
 
+def test_attention_tail_plan_sizes(pf):
+    # The workspace holds one partial slot (256 x 128 fp32 U, then m and l) per
+    # key segment of the tail units. Without a GPU the library plans for 256
+    # resident workgroups (one per CU of an MI355X). After floor(U / 256) whole
+    # rounds, full tail units and the heads' partial last units (n_q % 256
+    # queries) each get one segment count; a partial unit with at most four
+    # live waves counts 3/4 of a full unit per key tile, and segments hold at
+    # least 16 key tiles.
+    slot = (256 * 128 + 2 * 256) * 4
+    ws = pf.lib.pf_partition_attn_workspace_bytes
+    # 6240 q x 12 heads: 24 full + 1 partial (96 q, 3 live waves) units per head,
+    # 300 units: 256 whole, then 32 full x 6 segments + 12 partial x 5
+    assert ws(6240, 12, 27872) == (32 * 6 + 12 * 5) * slot
+    # 1100 q x 7 heads: 28 full units x 7 segments + 7 partial (76 q) x 6
+    assert ws(1100, 7, 20000) == (28 * 7 + 7 * 6) * slot
+    # 6300 q: partial units with 156 q (five live waves) cost as much as full
+    # ones; 47 key tiles allow two segments of each
+    assert ws(6300, 12, 6000) == (32 * 2 + 12 * 2) * slot
+    # 6144 q: no partial units; 32 tail units x 8 segments
+    assert ws(6144, 12, 27872) == 32 * 8 * slot
+    # 24 key tiles: too short to cut, the tail units run whole (no workspace)
+    assert ws(6300, 12, 3000) == 0
+
+
 def test_binding_rejects_cpu_tensors(pf):
     import torch
     q = torch.zeros(4, 2, 128, dtype=torch.bfloat16)

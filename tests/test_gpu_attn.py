@@ -225,6 +225,30 @@ def test_attn_whole_rounds_and_tail_only_plans():
         _compare(c, 9, [3, 0], rows=_sample_rows(n_q, H, extra=16), label=f"H={H} n_q={n_q}")
 
 
+@pytest.mark.parametrize("n_q,H,n_keys", [(3136, 20, 4000), (1100, 7, 20000), (6300, 12, 6000), (100, 5, 3000)],
+                         ids=["partial-units-in-round-and-tail", "two-kinds-7-and-6-segments",
+                              "five-live-waves", "one-partial-unit-per-head"])
+def test_attn_tail_plans_with_partial_query_units(n_q, H, n_keys):
+    # n_q not a multiple of 256: each head's last query unit is partial and its
+    # waves past n_q only load. With 256 resident workgroups these shapes put
+    # partial units in a whole round and in a tail of their own (3136 x 20),
+    # cut full and partial tail units into 7 and 6 key segments (1100 x 7),
+    # give partial units five live waves (6300 x 12), and leave no full unit
+    # (100 x 5); on any machine they cover partial units with 1..8 live waves
+    say(f"test_attn_tail_plans_with_partial_query_units n_q={n_q} H={H} keys={n_keys}")
+    rng = np.random.default_rng(n_q + H)
+    n_c, ids = 100, [7, 2, 11, 4]
+    n_sink, n_rec = 256, 300
+    n_cur = n_keys - n_sink - n_rec - len(ids) * n_c
+    c = dict(q=_bits(rng, n_q, H, 0.7), sink_k=_bits(rng, n_sink, H, 0.7), sink_v=_bits(rng, n_sink, H, 0.7),
+             pool_k=_bits(rng, 12 * n_c, H, 0.7), pool_v=_bits(rng, 12 * n_c, H, 0.7),
+             recent_k=_bits(rng, n_rec, H, 0.7), recent_v=_bits(rng, n_rec, H, 0.7),
+             cur_k=_bits(rng, n_cur, H, 0.7), cur_v=_bits(rng, n_cur, H, 0.7))
+    rows = _sample_rows(n_q, n_q, extra=24)
+    rows = np.union1d(rows, np.arange(max(0, n_q - 40), n_q))
+    _compare(c, n_c, ids, rows=rows, label=f"n_q={n_q} H={H} keys={n_keys}")
+
+
 @pytest.mark.parametrize("boost", [20.0, 70.0])
 def test_attn_late_dominant_keys(boost):
     # a few keys near the end of the context score `boost` nats above the rest:
