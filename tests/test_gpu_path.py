@@ -43,6 +43,8 @@ def check_step(label, cfg, c_ref, tags_ref, dl, out, rows):
     fr = (cfg.sink_blocks + c_ref["pool_k"].shape[0] // cfg.n_c) * cfg.block_frames
     ref = O.layer_step(c_ref, tags_ref, cfg.n_c, cfg.top_k, fr, cfg.block_frames, q_rows=rows)
     ids = ids.cpu().numpy().tolist()
+    # exact ranking of the scores the call returned, near-ties included
+    assert ids == O.select_topk(scores.cpu().numpy().astype(np.float64), cfg.top_k)
     flagged = ref["gap"] < 1e-3
     if ids != ref["ids"]:
         assert flagged and O.topk_acceptable(ids, ref["scores"], cfg.top_k, 1e-3), (ids, ref["ids"])
@@ -116,7 +118,7 @@ def test_full_generation_step_c3():
         qs = [pfgen.step_queries(cfg, l, step) for l in range(L)]
         q_dev = dev(np.stack(qs))
         view_k = pool_k_dev[:, :n_blocks * n_c]
-        ids, _ = pf.pf_score_select_batched(q_dev, view_k, n_c, k)
+        ids, sc = pf.pf_score_select_batched(q_dev, view_k, n_c, k)
         deltas = pf.pf_selection_deltas_batched(ids, tags_dev, fr, Bf)
         pf.pf_rope_shift_batched(view_k, n_c, deltas, ids)
         outs = {}
@@ -126,6 +128,9 @@ def test_full_generation_step_c3():
                                            pool_v_dev[l, :n_blocks * n_c], n_c, ids[l], d["recent_k"],
                                            d["recent_v"], d["cur_k"], d["cur_v"])[0]
         ids_h, deltas_h, tags_h = ids.cpu().numpy(), deltas.cpu().numpy(), tags_dev.cpu().numpy()
+        sc_h = sc.cpu().numpy().astype(np.float64)
+        for l in range(L):   # exact ranking of each layer's returned scores
+            assert ids_h[l].tolist() == O.select_topk(sc_h[l], k), (step, l)
         pools_h = {l: host(pool_k_dev[l, :n_blocks * n_c]) for l in range(L) if l not in diverged}
         o_h = {l: host(outs[l])[rows] for l in attn_layers}
 

@@ -29,6 +29,9 @@ def _compare(c, n_c, k, require_unflagged=False):
         f"k/k+1 gap {gap:.3e}{' FLAGGED' if flagged else ''}")
     assert err <= 1e-5 + 1e-5 * float(np.max(np.abs(ref_s)))
     assert ids == sorted(ids) and len(set(ids)) == k
+    # the ranking is exact at every size, near-ties included: the ids are the
+    # top-k of the scores the call returned, by (-score, index)
+    assert ids == O.select_topk(s, k)
     if require_unflagged:
         assert not flagged
     if flagged:
@@ -176,6 +179,7 @@ def test_select_subsampled(steps):
     gap = O.topk_gap(ref_s, cfg.top_k)
     say(f"  score max-abs err {err:.2e}, k/k+1 gap {gap:.3e}")
     assert err <= 1e-5 + 1e-5 * float(np.max(np.abs(ref_s)))
+    assert ids == O.select_topk(s, cfg.top_k)
     if gap >= FLAG_GAP:
         assert ids == O.select_topk(ref_s, cfg.top_k)
     else:
@@ -232,6 +236,7 @@ def test_select_place_batched_equals_single_calls(B):
         assert d[b].cpu().numpy().tolist() == d1.cpu().numpy().tolist()
         assert np.array_equal(s[b].cpu().numpy().view(np.uint32), s1.cpu().numpy().view(np.uint32))
         assert tags[b].cpu().numpy().tolist() == t1.cpu().numpy().tolist()
+        assert ids[b].cpu().numpy().tolist() == O.select_topk(s[b].cpu().numpy().astype(np.float64), k)
 
 
 def test_random_selector_matches_oracle_bit_exact():
