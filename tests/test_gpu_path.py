@@ -93,7 +93,10 @@ def test_full_generation_step_c3():
     L, S, M, n_c, k, Bf, H = cfg.layers, cfg.steps, cfg.pool_blocks, cfg.n_c, cfg.top_k, cfg.block_frames, cfg.heads
     Sb = cfg.sink_blocks
     attn_layers = (0, L // 2, L - 1)
-    rows = np.unique(np.r_[0, 127, 128, cfg.n - 1, np.random.default_rng(1).integers(0, cfg.n, 4)])
+    # unit edges, and the last (partial) 256-query unit of a head, whose waves
+    # past the last query only load
+    rows = np.unique(np.r_[0, 127, 128, 255, 256, cfg.n - 96, cfg.n - 33, cfg.n - 1,
+                           np.random.default_rng(1).integers(0, cfg.n, 8)])
     say(f"test_full_generation_step_c3: {L} layers x {S} steps, pool {M} -> {M + 1}")
 
     pool_rows = (M + 1) * n_c
