@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (the 2.5 PFLOP/s figure)
 PEAK_HBM_GBS = 8000.0
+SETTLE_STEPS = 15          # untimed layer-steps before any timing, whatever --warmup says
 PMC_FILE = os.path.join(ROOT, "profiles", "partition_attn_default_hbm_counters.json")
 
 
@@ -666,16 +667,18 @@ def main():
                              t["recent_k"], t["recent_v"], t["cur_k"], t["cur_v"], o=o, workspace=aws)
         if ev: ev[3].record(stream)
 
-    for i in range(args.warmup):
+    # the clock takes about a dozen attention launches to settle: the untimed
+    # warm-up is topped up to SETTLE_STEPS layer-steps before anything is timed
+    n_warm = max(args.warmup, SETTLE_STEPS)
+    for i in range(n_warm):
         step(i)
     torch.cuda.synchronize()
 
     # K steps with an event after each call, for the per-call breakdown and the
-    # spread of step times (the clock takes about a dozen attention launches to
-    # settle, so these also run before the headline steps)
+    # spread of step times (these also run before the headline steps)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(n_warm + i, evs[i])
     torch.cuda.synchronize()
     part = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])   # [steps, 3] ms
     ms_select, ms_rope, ms_attn = part.mean(axis=0)
@@ -687,7 +690,7 @@ def main():
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + args.steps + i)
+        step(n_warm + args.steps + i)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
@@ -708,6 +711,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_layer_steps_run": n_warm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
