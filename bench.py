@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-c4", action="store_true", help="skip the unbounded 748,800-key contrast")
     ap.add_argument("--layer-step-only", action="store_true",
                     help="only the warm-up and timed layer-steps (for profiling their kernels)")
+    ap.add_argument("--c4-only", action="store_true",
+                    help="time only the unbounded 748,800-key attention (for profiling it)")
     ap.add_argument("--hr-only", action="store_true",
                     help="time only the HR-branch compressor (for profiling its kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -624,6 +626,10 @@ def main():
 
     if args.batched_only:
         print(json.dumps({"hbm_batched": hbm_batched(pf, torch, pfgen.C2, pfgen.C3.layers, args.steps)}), flush=True)
+        return
+    if args.c4_only:
+        print(json.dumps({"unbounded_c4": unbounded_c4(pf, torch, pfgen.C4, cpu=False, reps=args.steps)}),
+              flush=True)
         return
     if args.hr_only:
         def dev_bits(a):
